@@ -1,0 +1,29 @@
+"""Build the oracle's shared library (oracle/liboracle.so) with gcc.
+
+Test infrastructure: the library built here is loaded only by the test suite,
+the smoke check and the benchmark's CPU-baseline leg.  No fast-math and no
+vector intrinsics: the oracle is meant to be read, not to be fast.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "mxfp4_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle; returns the library path."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force="--lazy" not in sys.argv))

@@ -1,0 +1,265 @@
+"""Pins for the CPU oracle, against facts that do not come from the oracle itself.
+
+Each test checks the oracle against something independent of its own code:
+hand-worked fixed points from the pages' rules (tests/golden/), an
+independently derived formulation swept over every bf16 value, closed forms
+of the product, brute force with a library matmul, and error bounds.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_precision_quant_amd import inputs
+from conftest import read_golden
+
+# ---------------------------------------------------------------- helpers
+
+
+def bf16_of(values):
+    """bf16 bit patterns of values that are exactly representable in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    bits = f.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "fixture value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def all_finite_bf16():
+    """Every finite bf16 bit pattern (both signs), as uint16."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (h >> 7) & 0xFF
+    return h[exp != 0xFF]
+
+
+def codes_by_binade(x64):
+    """e2m1 code magnitudes by an independent route: round-half-even of x in
+    units of the grid spacing of its binade (0.5 below 2, 1 in [2, 4), 2 in
+    [4, 6)), then offset by the code index of the binade's first value;
+    saturate at 6.  Written from the e2m1 value grid, not from the oracle."""
+    a = np.abs(x64)
+    c = np.where(a < 2.0, np.rint(a * 2.0),
+                 np.where(a < 4.0, np.rint(a) + 2.0,
+                          np.where(a < 6.0, np.rint(a * 0.5) + 4.0, 7.0)))
+    return np.minimum(c, 7.0).astype(np.uint8)
+
+
+def golden_table():
+    table = {}
+    for line in read_golden("e2m1_codes.txt"):
+        c, v = line.split()
+        table[int(c)] = float(v)
+    return table
+
+
+def decode_with_table(fp4, scale):
+    """Dequantize with the fixture's code table and numpy only."""
+    t = golden_table()
+    lut = np.array([t[c] for c in range(16)], dtype=np.float64)
+    rows, half = fp4.shape
+    codes = np.empty((rows, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = fp4 & 0x0F
+    codes[:, 1::2] = fp4 >> 4
+    vals = lut[codes]
+    factor = np.exp2(scale.astype(np.float64) - 127.0)
+    return vals * np.repeat(factor, 32, axis=1)
+
+
+# ------------------------------------------------------- code table & rounding
+
+
+def test_code_table_values_and_roundtrip():
+    table = golden_table()
+    assert sorted(abs(v) for c, v in table.items() if c < 8) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for code, value in table.items():
+        got = oracle.dequant_value(code, 127)
+        assert got == value and math.copysign(1.0, got) == math.copysign(1.0, value), code
+        # requantize at unit scale: every code maps back to itself (-0.0 -> 8)
+        assert oracle.e2m1_code(value, 127) == code
+
+
+@pytest.mark.parametrize("line", read_golden("e2m1_rounding.txt"))
+def test_rounding_fixed_points(line):
+    x, byte, want = line.split()
+    assert oracle.e2m1_code(float(x), int(byte)) == int(want)
+
+
+@pytest.mark.parametrize("line", read_golden("scale_bytes.txt"))
+def test_scale_fixed_points(line):
+    amax, want = line.split()
+    assert oracle.scale_byte(float(np.float32(float(amax)))) == int(want)
+
+
+def test_scale_rule_exhaustive_vs_frexp():
+    """Every finite non-negative bf16 as a group maximum: the oracle's bit rule
+    equals floor(log2 amax) + [significand >= 1.75] - 2, clamped, biased."""
+    h = all_finite_bf16()
+    h = h[h < 0x8000]
+    vals = inputs.bf16_bits_to_f32(h)
+    for bits, v in zip(h.tolist(), vals.tolist()):
+        if v == 0.0:
+            want = 0
+        else:
+            mant, ex = math.frexp(v)  # v = mant * 2^ex, mant in [0.5, 1)
+            e = ex - 1
+            if 2.0 * mant >= 1.75:
+                e += 1
+            want = min(max(e - 2, -127), 127) + 127
+        assert oracle.scale_byte(v) == want, hex(bits)
+
+
+def test_element_code_exhaustive_vs_binade_rounding():
+    """Every finite bf16 value under every scale byte 0..254: the oracle's
+    nearest-value search equals the per-binade half-even rounding."""
+    h = all_finite_bf16()
+    x = inputs.bf16_bits_to_f32(h)
+    sign = ((h >> 15) & 1).astype(np.uint8) << 3
+    for byte in range(255):
+        got = oracle.e2m1_codes(x, np.int32(byte))
+        q = x.astype(np.float64) * 2.0 ** (127 - byte)
+        want = codes_by_binade(q) | sign
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (byte, hex(int(h[bad[0]])), int(got[bad[0]]), int(want[bad[0]]))
+
+
+# ------------------------------------------------------------- whole groups
+
+
+def _parse_values(spec):
+    out = []
+    for tok in spec.split():
+        if "*" in tok:
+            v, n = tok.split("*")
+            out += [float(v)] * int(n)
+        else:
+            out.append(float(tok))
+    assert len(out) == 32
+    return out
+
+
+@pytest.mark.parametrize("line", read_golden("groups.txt"))
+def test_group_fixed_points(line):
+    name, vals, byte, packed = [p.strip() for p in line.split("|")]
+    x = bf16_of(_parse_values(vals)).reshape(1, 32)
+    q, s = oracle.quantize(x)
+    assert int(s[0, 0]) == int(byte), name
+    assert q[0].tolist() == [int(b, 16) for b in packed.split()], name
+
+
+def test_quantize_rows_matches_elementwise_rule():
+    """quantize() = scale rule per group + code rule per element + nibble packing."""
+    a, _ = inputs.make_shape(3, 16, 256, seed=11)
+    q, s = oracle.quantize(a)
+    x = inputs.bf16_bits_to_f32(a).reshape(3, 8, 32)
+    amax = np.abs(x).max(axis=2)
+    for r in range(3):
+        for g in range(8):
+            assert s[r, g] == oracle.scale_byte(float(amax[r, g]))
+    codes = oracle.e2m1_codes(x.reshape(-1), np.repeat(s.reshape(-1).astype(np.int32), 32))
+    codes = codes.reshape(3, 256)
+    assert np.array_equal(q, codes[:, 0::2] | (codes[:, 1::2] << 4))
+
+
+def test_quantization_error_bound():
+    """Non-saturated elements are within half a grid step of their code value;
+    saturated ones sit at 6 * 2^s with |x| < 7 * 2^s (significand < 1.75)."""
+    a, _ = inputs.make_shape(8, 16, 1024, seed=12)
+    a[0, 0] = bf16_of([1.625])[0]  # significand in [1.5, 1.75): saturates by design
+    a[0, 1:32] = bf16_of([0.25] * 31)
+    q, s = oracle.quantize(a)
+    x = inputs.bf16_bits_to_f32(a).astype(np.float64)
+    d = oracle.dequantize(q, s)
+    unit = np.repeat(np.exp2(s.astype(np.float64) - 127.0), 32, axis=1)
+    qx = np.abs(x) / unit
+    step = np.where(qx < 2, 0.5, np.where(qx < 4, 1.0, 2.0))
+    sat = qx >= 6
+    err = np.abs(x - d) / unit
+    assert np.all(err[~sat] <= step[~sat] / 2 + 1e-12)
+    assert np.all(np.abs(d[sat]) / unit[sat] == 6.0)
+    assert np.all(qx < 7.0)
+
+
+def test_group_scale_invariance():
+    """Scaling a group by 2^t shifts its scale byte by t and keeps its codes."""
+    a, _ = inputs.make_shape(4, 16, 128, seed=13)
+    x = inputs.bf16_bits_to_f32(a)
+    q0, s0 = oracle.quantize(a)
+    for t in (-20, -3, 1, 5, 30):
+        at = inputs.f32_to_bf16_bits(x * np.float32(2.0 ** t))
+        qt, st = oracle.quantize(at)
+        assert np.array_equal(qt, q0)
+        assert np.array_equal(st.astype(int), s0.astype(int) + t)
+
+
+# --------------------------------------------------------------- dequantize
+
+
+def test_dequantize_matches_table_decode():
+    a, _ = inputs.make_shape(5, 16, 512, seed=14)
+    q, s = oracle.quantize(a)
+    assert np.array_equal(oracle.dequantize(q, s), decode_with_table(q, s))
+
+
+def test_unit_scale_byte():
+    for code in range(16):
+        for t in (-5, 0, 7):
+            assert oracle.dequant_value(code, 127 + t) == golden_table()[code] * 2.0 ** t
+
+
+# --------------------------------------------------------------------- gemm
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 32, 1), (3, 5, 64, 2), (8, 16, 128, 3),
+                                         (16, 16, 256, 4), (7, 9, 96, 5)])
+def test_gemm_brute_force_vs_matmul(M, N, K, seed):
+    a, b = inputs.make_shape(M, N, K, seed=seed)
+    ref = oracle.reference(a, b, want64=True)
+    ad = decode_with_table(ref["aq"], ref["as"])
+    bd = decode_with_table(ref["bq"], ref["bs"])
+    exact = ad @ bd.T
+    np.testing.assert_allclose(ref["c64"], exact, rtol=1e-12, atol=1e-12)
+    bound = K * 2.0 ** -24 * oracle.gemm_abs(ad, bd) + 1e-30
+    assert np.all(np.abs(ref["c32"].astype(np.float64) - ref["c64"]) <= bound)
+
+
+def test_gemm_transposition_and_one_hot():
+    """A one-hot row picks column k of B: C[m, n] = deqB[n, k]."""
+    M, N, K = 4, 16, 128
+    _, b = inputs.make_shape(M, N, K, seed=21)
+    ks = [0, 37, 64, 127]
+    a = np.zeros((M, K), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        a[m, k] = bf16_of([1.0])[0]
+    ref = oracle.reference(a, b)
+    bd = decode_with_table(ref["bq"], ref["bs"])
+    for m, k in enumerate(ks):
+        assert np.array_equal(ref["c32"][m].astype(np.float64), bd[:, k])
+
+
+def test_gemm_all_ones_is_row_sum():
+    M, N, K = 2, 16, 256
+    _, b = inputs.make_shape(M, N, K, seed=22)
+    a = np.full((M, K), bf16_of([1.0])[0], dtype=np.uint16)
+    ref = oracle.reference(a, b, want64=True)
+    bd = decode_with_table(ref["bq"], ref["bs"])
+    np.testing.assert_array_equal(ref["c64"], np.tile(bd.sum(axis=1), (M, 1)))
+
+
+def test_gemm_b_scale_shift():
+    """Scaling B by 2^t scales C by exactly 2^t."""
+    M, N, K = 4, 16, 256
+    a, b = inputs.make_shape(M, N, K, seed=23)
+    c0 = oracle.reference(a, b)["c32"]
+    bt = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(b) * np.float32(8.0))
+    c3 = oracle.reference(a, bt)["c32"]
+    np.testing.assert_array_equal(c3, c0 * np.float32(8.0))
+
+
+def test_workload_inputs_are_seeded():
+    a1, b1 = inputs.make("m4_n2880_k512")
+    a2, b2 = inputs.make("m4_n2880_k512")
+    assert a1.shape == (4, 512) and b1.shape == (2880, 512)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+    a3, _ = inputs.make("m16_n2112_k7168")
+    big = np.abs(inputs.bf16_bits_to_f32(a3)) > 8
+    assert 1000 < big.sum() <= 1147 + 5
