@@ -1,0 +1,230 @@
+"""Benchmark: L2-cold microseconds per MXFP4 GEMM call on one MI355X.
+
+Default workload: the two M=32, K=512 shapes (N=4096 and N=2880).  One step
+is one call of each shape; before every timed call a 512 MiB device fill
+evicts the L2 caches and the Infinity Cache, and HIP events on the launch
+stream bracket the call alone.  Inputs (A bf16, packed B) are resident in
+HBM before timing starts; B is quantized by the library's own quantizer and
+repacked once (reported separately as prepack_us).
+
+Prints one JSON line.  `value` is the mean over the workload's shapes of the
+median L2-cold event time per call (µs, lower is better).  `ms_per_step`
+is wall time per step including the cache-evicting fills.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+                  [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_scaled_precision_quant_amd import inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0
+FLUSH_BYTES = 512 << 20
+
+WORKLOAD_SETS = {
+    "m32_k512": ["m32_n4096_k512", "m32_n2880_k512"],
+}
+for _n in inputs.ORDER:
+    WORKLOAD_SETS[_n] = [_n]
+
+
+def alg_bytes(M, N, K):
+    """Bytes the method itself must move per call: A bf16, B fp4 + e8m0, C bf16."""
+    return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="m32_k512", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--all", action="store_true", help="one extra JSON line per tuned shape")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+class Case:
+    """Device-resident inputs and outputs of one shape."""
+
+    def __init__(self, name, torch, mx):
+        w = inputs.WORKLOADS[name]
+        self.name, self.M, self.N, self.K = name, w.M, w.N, w.K
+        a_bits, b_bits = inputs.make(name)
+        dev = torch.device("cuda:0")
+        to = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.a = to(a_bits)
+        b = to(b_bits)
+        self.bq, self.bs = mx.quant_a(b)  # the library's quantizer on B's rows
+        self.b_packed = torch.empty(mx.packed_bytes(self.N, self.K), dtype=torch.uint8, device=dev)
+        self.c = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+        self.plan = mx.default_plan(self.M, self.N, self.K)
+        nws = mx.workspace_bytes(self.M, self.N, self.K)
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) if nws else None
+        self.mx = mx
+        mx.pack_b(self.bq, self.bs, out=self.b_packed)
+        torch.cuda.synchronize()
+
+    def pack(self):
+        self.mx.pack_b(self.bq, self.bs, out=self.b_packed)
+
+    def call(self):
+        self.mx.gemm(self.a, self.b_packed, self.N, out=self.c, workspace=self.ws, plan=self.plan)
+
+
+def time_cold(torch, flush, fn, steps, warmup):
+    """Median/mean µs of fn() with an L2 + Infinity Cache eviction before each call."""
+    for _ in range(warmup):
+        flush.zero_()
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        flush.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1000.0 for a, b in evs]
+    return us
+
+
+def cpu_baseline(names, seconds):
+    """The oracle as it stands (single thread), on the same inputs: quantize A,
+    dequantize A and B, fp32 dot.  B's quantization is excluded, as it is in
+    the GPU call (B arrives pre-quantized)."""
+    import oracle
+    prepared = []
+    for n in names:
+        a, b = inputs.make(n)
+        bq, bs = oracle.quantize(b)
+        prepared.append((a, bq, bs))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for a, bq, bs in prepared:
+            aq, asc = oracle.quantize(a)
+            ad = oracle.dequantize(aq, asc)
+            bd = oracle.dequantize(bq, bs)
+            oracle.gemm(ad, bd, want64=False)
+            calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": dt / calls * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": "%d full oracle calls over the workload's shapes (%s), %.1f s, 1 thread"
+                      % (calls, ", ".join(names), dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(N-sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_precision_quant_amd as mx
+
+    names = WORKLOAD_SETS[args.workload]
+    cases = [Case(n, torch, mx) for n in names]
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+
+    # timed region: K steps, each one cold call per shape
+    for _ in range(args.warmup):
+        for c in cases:
+            flush.zero_()
+            c.call()
+    torch.cuda.synchronize()
+    ev = {c.name: [] for c in cases}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in cases:
+            flush.zero_()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c.call()
+            e1.record()
+            ev[c.name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {}
+    for c in cases:
+        us = [a.elapsed_time(b) * 1000.0 for a, b in ev[c.name]]
+        per[c.name] = {"median_us": statistics.median(us), "mean_us": statistics.fmean(us),
+                       "min_us": min(us), "plan": c.plan.__dict__,
+                       "alg_bytes": alg_bytes(c.M, c.N, c.K), "flops": 2 * c.M * c.N * c.K}
+    value = statistics.fmean(p["median_us"] for p in per.values())
+
+    # dominant kernel: the GEMM kernel; with single-launch plans the event pair
+    # brackets exactly that kernel
+    tot_bytes = sum(p["alg_bytes"] for p in per.values())
+    tot_us = sum(p["median_us"] for p in per.values())
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    tot_flops = sum(p["flops"] for p in per.values())
+    for c in cases:
+        p = per[c.name]
+        p["hbm_GBps"] = p["alg_bytes"] / (p["median_us"] * 1e-6) / 1e9
+        p["hbm_frac"] = p["hbm_GBps"] / HBM_PEAK_GBPS
+        p["mfma_frac"] = p["flops"] / (p["median_us"] * 1e-6) / 1e12 / FP4_PEAK_TFLOPS
+        p["prepack_us"] = statistics.median(time_cold(torch, flush, c.pack, 10, 2))
+
+    line = {
+        "metric": "L2-cold us/call per (M,N,K) + achieved HBM TB/s and FP4 MFMA % of peak",
+        "value": round(value, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4(e2m1)+e8m0 x fp4 -> fp32 acc, bf16 in/out",
+        "data": "synthetic (seeded normal A and B, bf16)",
+        "config": {"workload": "mxfp4_gemm " + " + ".join(
+            "M=%d N=%d K=%d" % (c.M, c.N, c.K) for c in cases), "shapes": per},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "hbm_TBps": round(achieved / 1000.0, 4),
+        "mfma_frac_fp4": round(tot_flops / (tot_us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(names, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        for n in inputs.ORDER:
+            c = Case(n, torch, mx)
+            us = time_cold(torch, flush, c.call, args.steps, args.warmup)
+            med = statistics.median(us)
+            b = alg_bytes(c.M, c.N, c.K)
+            print(json.dumps({"shape": n, "plan": c.plan.__dict__, "median_us": round(med, 3),
+                              "mean_us": round(statistics.fmean(us), 3),
+                              "hbm_GBps": round(b / (med * 1e-6) / 1e9, 1),
+                              "mfma_frac_fp4": round(2 * c.M * c.N * c.K / (med * 1e-6) / 1e12
+                                                     / FP4_PEAK_TFLOPS, 5),
+                              "prepack_us": round(statistics.median(
+                                  time_cold(torch, flush, c.pack, 10, 2)), 3)}), flush=True)
+            del c
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+"""MXFP4 GEMM for MI355X (gfx950): Python binding of libmxfp4.so.
+
+C[M, N] = A[M, K] . B[N, K]^T with bf16 output; A is bf16 and quantized on the
+fly to MXFP4 (e2m1 codes, one e8m0 scale per 32 K-elements), B is quantized
+once and repacked into the kernels' layout.
+
+This module only marshals arguments: tensors become device pointers, the
+current torch stream becomes the HIP stream, and every computation runs in
+the library's HIP kernels.  There is no fallback path: if the library is
+missing or a call fails, an exception is raised.  The C functions and their
+contracts are declared in include/mxfp4.h.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "library_path", "load", "packed_bytes",
+    "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "gemm",
+    "gemm_prequant", "version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+MODE_FUSED = 1
+MODE_PREQUANT = 2
+
+_ERR_NAMES = {-1: "EINVAL", -2: "ENULL", -3: "EWORKSPACE", -4: "ESIZE", -5: "ENOTSUP", -6: "EHIP"}
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__("mxfp4 %s (%d): %s" % (_ERR_NAMES.get(code, "?"), code, message))
+        self.code = code
+
+
+class _CPlan(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("m_blocks", ctypes.c_int),
+                ("n_tiles_per_wave", ctypes.c_int), ("waves_n", ctypes.c_int),
+                ("waves_k", ctypes.c_int), ("k_steps_per_wave", ctypes.c_int),
+                ("split_k", ctypes.c_int)]
+
+
+@dataclass(frozen=True)
+class Plan:
+    """Tiling of one GEMM call (fields as in mxfp4_plan)."""
+    mode: int
+    m_blocks: int
+    n_tiles_per_wave: int
+    waves_n: int
+    waves_k: int
+    k_steps_per_wave: int
+    split_k: int
+
+    def _c(self):
+        return _CPlan(self.mode, self.m_blocks, self.n_tiles_per_wave, self.waves_n, self.waves_k,
+                      self.k_steps_per_wave, self.split_k)
+
+
+_LIB = None
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i = ctypes.c_int
+
+# name -> (restype, argtypes); every symbol the header declares
+_SIGNATURES = {
+    "mxfp4_packed_bytes": (_sz, [_i, _i]),
+    "mxfp4_pack_b": (_i, [_vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "mxfp4_quant_a": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]),
+    "mxfp4_quant_a_packed": (_i, [_vp, _i, _i, _i, _vp, _sz, _vp]),
+    "mxfp4_default_plan": (_i, [_i, _i, _i, ctypes.POINTER(_CPlan)]),
+    "mxfp4_check_plan": (_i, [ctypes.POINTER(_CPlan), _i, _i, _i]),
+    "mxfp4_plan_workspace_bytes": (_sz, [ctypes.POINTER(_CPlan), _i, _i, _i]),
+    "mxfp4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
+    "mxfp4_gemm": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "mxfp4_gemm_ex": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz,
+                           ctypes.POINTER(_CPlan), _vp]),
+    "mxfp4_gemm_prequant": (_i, [_vp, _sz, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz,
+                                 ctypes.POINTER(_CPlan), _vp]),
+    "mxfp4_last_error": (ctypes.c_char_p, []),
+    "mxfp4_version": (ctypes.c_char_p, []),
+}
+
+
+def library_path():
+    return os.path.join(_PKG, "libmxfp4.so")
+
+
+def load():
+    """Load libmxfp4.so (built by __graft_entry__.build()); raises if absent."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError("libmxfp4.so is not built (%s); run __graft_entry__.build()" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(rc):
+    if rc != 0:
+        raise Mxfp4Error(rc, load().mxfp4_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def version():
+    return load().mxfp4_version().decode()
+
+
+def packed_bytes(rows, K):
+    """Bytes of the MX-packed layout of `rows` x K (0 if invalid)."""
+    return int(load().mxfp4_packed_bytes(int(rows), int(K)))
+
+
+def pack_b(b_fp4, b_scale, out=None, stream=None):
+    """Repack linear fp4x2 [N, K/2] + e8m0 [N, K/32] (uint8 CUDA tensors) into
+    the MX-packed layout; returns the uint8 buffer."""
+    import torch
+    N, half = b_fp4.shape
+    K = 2 * half
+    if out is None:
+        out = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=b_fp4.device)
+    _check(load().mxfp4_pack_b(_ptr(b_fp4), _ptr(b_scale), N, K, _ptr(out), _nbytes(out),
+                               _stream(stream)))
+    return out
+
+
+def _rows(a):
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("A must be a 2-D tensor with unit stride along K")
+    return a.shape[0], a.shape[1], a.stride(0)
+
+
+def quant_a(a, out_fp4=None, out_scale=None, stream=None):
+    """Quantize bf16 [M, K] to linear fp4x2 [M, K/2] + e8m0 [M, K/32]."""
+    import torch
+    M, K, lda = _rows(a)
+    if out_fp4 is None:
+        out_fp4 = torch.empty((M, K // 2), dtype=torch.uint8, device=a.device)
+    if out_scale is None:
+        out_scale = torch.empty((M, K // 32), dtype=torch.uint8, device=a.device)
+    _check(load().mxfp4_quant_a(_ptr(a), M, K, lda, _ptr(out_fp4), out_fp4.stride(0),
+                                _ptr(out_scale), out_scale.stride(0), _stream(stream)))
+    return out_fp4, out_scale
+
+
+def quant_a_packed(a, out=None, stream=None):
+    """Quantize bf16 [M, K] straight into the MX-packed layout."""
+    import torch
+    M, K, lda = _rows(a)
+    if out is None:
+        out = torch.empty(packed_bytes(M, K), dtype=torch.uint8, device=a.device)
+    _check(load().mxfp4_quant_a_packed(_ptr(a), M, K, lda, _ptr(out), _nbytes(out),
+                                       _stream(stream)))
+    return out
+
+
+def default_plan(M, N, K):
+    p = _CPlan()
+    _check(load().mxfp4_default_plan(M, N, K, ctypes.byref(p)))
+    return Plan(p.mode, p.m_blocks, p.n_tiles_per_wave, p.waves_n, p.waves_k,
+                p.k_steps_per_wave, p.split_k)
+
+
+def check_plan(plan, M, N, K):
+    """Raise Mxfp4Error unless `plan` is valid for the shape in this build."""
+    cp = plan._c()
+    _check(load().mxfp4_check_plan(ctypes.byref(cp), M, N, K))
+
+
+def workspace_bytes(M, N, K, plan=None):
+    if plan is None:
+        return int(load().mxfp4_gemm_workspace_bytes(M, N, K))
+    cp = plan._c()
+    return int(load().mxfp4_plan_workspace_bytes(ctypes.byref(cp), M, N, K))
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def gemm(a, b_packed, N, out=None, workspace=None, plan=None, stream=None):
+    """C = A . B^T: A bf16 [M, K] (CUDA), b_packed from pack_b for N rows.
+    Returns bf16 [M, N] (written into `out` when given)."""
+    import torch
+    M, K, lda = _rows(a)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    workspace = _workspace(workspace_bytes(M, N, K, plan), a.device, workspace)
+    cp = plan._c() if plan is not None else None
+    _check(load().mxfp4_gemm_ex(_ptr(a), lda, _ptr(b_packed), _nbytes(b_packed), _ptr(out),
+                                out.stride(0), M, N, K, _ptr(workspace),
+                                _nbytes(workspace) if workspace is not None else 0,
+                                ctypes.byref(cp) if cp is not None else None, _stream(stream)))
+    return out
+
+
+def gemm_prequant(a_packed, M, b_packed, N, K, out=None, workspace=None, plan=None, stream=None):
+    """C = A . B^T with A already MX-packed (from quant_a_packed)."""
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_packed.device)
+    p = plan if plan is not None else default_plan(M, N, K)
+    need = p.split_k * M * N * 4 if p.split_k > 1 else 0
+    workspace = _workspace(need, a_packed.device, workspace)
+    cp = p._c()
+    _check(load().mxfp4_gemm_prequant(_ptr(a_packed), _nbytes(a_packed), _ptr(b_packed),
+                                      _nbytes(b_packed), _ptr(out), out.stride(0), M, N, K,
+                                      _ptr(workspace),
+                                      _nbytes(workspace) if workspace is not None else 0,
+                                      ctypes.byref(cp), _stream(stream)))
+    return out

@@ -1,0 +1,356 @@
+// api.cpp -- the extern "C" boundary of libmxfp4.so: argument checks, plan
+// selection, workspace carving and launches.  Every check happens before
+// anything is enqueued, so an error other than MXFP4_EHIP leaves the stream
+// untouched.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/mxfp4.h"
+#include "mx_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MXFP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MXFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+mx::Plan to_internal(const mxfp4_plan& p) {
+  mx::Plan q;
+  q.mode = p.mode;
+  q.mbw = p.m_blocks;
+  q.ntw = p.n_tiles_per_wave;
+  q.wn = p.waves_n;
+  q.wk = p.waves_k;
+  q.ksw = p.k_steps_per_wave;
+  q.split = p.split_k;
+  return q;
+}
+
+mxfp4_plan make_plan(int mode, int mbw, int ntw, int wn, int wk, int ksw, int split) {
+  mxfp4_plan p;
+  p.mode = mode;
+  p.m_blocks = mbw;
+  p.n_tiles_per_wave = ntw;
+  p.waves_n = wn;
+  p.waves_k = wk;
+  p.k_steps_per_wave = ksw;
+  p.split_k = split;
+  return p;
+}
+
+int check_gemm_shape(int M, int N, int K) {
+  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
+  if (N < 16 || N % 16 != 0) return fail(MXFP4_EINVAL, "N must be a positive multiple of 16 (got %d)", N);
+  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  return MXFP4_OK;
+}
+
+// Checks a plan against a shape; `mode_matters` is false for the prequant
+// entry point, which ignores the mode field.
+int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
+  if (mode_matters && p.mode != MXFP4_MODE_FUSED && p.mode != MXFP4_MODE_PREQUANT)
+    return fail(MXFP4_EINVAL, "plan.mode must be MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT (got %d)", p.mode);
+  if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
+      p.k_steps_per_wave < 1 || p.split_k < 1)
+    return fail(MXFP4_EINVAL, "plan fields must all be >= 1");
+  const int mode = mode_matters ? p.mode : MXFP4_MODE_PREQUANT;
+  if (!mx::gemm_kernel_available(mode, p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave))
+    return fail(MXFP4_ENOTSUP,
+                "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this build",
+                p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
+  const int KS = K / 128;
+  if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
+    return fail(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal K/128)",
+                (long long)p.split_k * p.waves_k * p.k_steps_per_wave, KS);
+  if (p.waves_n * p.waves_k > mx::kMaxThreads / 64)
+    return fail(MXFP4_EINVAL, "plan has %d wavefronts per workgroup (max %d)", p.waves_n * p.waves_k,
+                mx::kMaxThreads / 64);
+  mx::Plan q = to_internal(p);
+  q.mode = mode;
+  const mx::GemmGeom g = mx::gemm_geometry(q, M, N, K);
+  if (g.lds_total > (size_t)mx::kMaxLds)
+    return fail(MXFP4_EINVAL, "plan needs %zu bytes of LDS (max %d)", g.lds_total, mx::kMaxLds);
+  if ((long long)g.mgroups * g.ngroups * p.split_k > 0x7FFFFFFFLL)
+    return fail(MXFP4_EINVAL, "grid too large");
+  return MXFP4_OK;
+}
+
+size_t plan_workspace(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
+  size_t bytes = 0;
+  if (!prequant_entry && p.mode == MXFP4_MODE_PREQUANT)
+    bytes += round_up(mxfp4_packed_bytes(M, K), 256);
+  if (p.split_k > 1) bytes += (size_t)p.split_k * M * N * 4;
+  return bytes;
+}
+
+// Per-shape table for the tuned shapes, heuristic otherwise.
+mxfp4_plan default_plan(int M, int N, int K) {
+  struct Row {
+    int M, N, K;
+    mxfp4_plan p;
+  };
+  static const Row table[] = {
+      {4, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 1, 1, 4, 1)},
+      {32, 4096, 512, make_plan(MXFP4_MODE_FUSED, 2, 1, 2, 1, 4, 1)},
+      {32, 2880, 512, make_plan(MXFP4_MODE_FUSED, 2, 1, 2, 1, 4, 1)},
+      {16, 2112, 7168, make_plan(MXFP4_MODE_PREQUANT, 1, 1, 1, 2, 7, 4)},
+      {64, 7168, 2048, make_plan(MXFP4_MODE_PREQUANT, 4, 1, 2, 1, 16, 1)},
+      {256, 3072, 1536, make_plan(MXFP4_MODE_PREQUANT, 4, 1, 4, 1, 12, 1)},
+  };
+  for (const Row& r : table)
+    if (r.M == M && r.N == N && r.K == K) return r.p;
+
+  // Heuristic: fused quantization for small M, prequant otherwise; the
+  // largest compiled per-wave step count that divides K/128 with at most 8
+  // workgroups along K; in-block split along K when the grid is thin.
+  const int KS = K / 128;
+  const int MT = (M + 15) / 16;
+  const int mode = M <= 32 ? MXFP4_MODE_FUSED : MXFP4_MODE_PREQUANT;
+  const int mbw = MT >= 4 ? 4 : (MT >= 2 ? 2 : 1);
+  static const int ksw_opts[] = {16, 14, 12, 8, 7, 6, 4, 3, 2, 1};
+  int ksw = 1;
+  for (int k : ksw_opts)
+    if (KS % k == 0 && KS / k <= 8) {
+      ksw = k;
+      break;
+    }
+  if (KS % ksw != 0 || KS / ksw > 8) {
+    for (int k : ksw_opts)
+      if (KS % k == 0) {
+        ksw = k;
+        break;
+      }
+  }
+  int rest = KS / ksw;  // split_k * waves_k
+  int wk = 1;
+  while (wk < 4 && rest % (wk * 2) == 0) wk *= 2;
+  mxfp4_plan p = make_plan(mode, mbw, 1, 2, wk, ksw, rest / wk);
+  // keep the workgroup's A stage within LDS: trade in-block K waves for
+  // workgroups along K, then smaller row blocks, then the prequant stage
+  for (;;) {
+    if (mx::gemm_geometry(to_internal(p), M, N, K).lds_total <= (size_t)mx::kMaxLds) break;
+    if (p.waves_k > 1) {
+      p.waves_k /= 2;
+      p.split_k *= 2;
+    } else if (p.m_blocks > 1) {
+      p.m_blocks /= 2;
+    } else if (p.mode == MXFP4_MODE_FUSED) {
+      p.mode = MXFP4_MODE_PREQUANT;
+    } else {
+      break;
+    }
+  }
+  return p;
+}
+
+int check_stream_ptrs(const void* p, const char* name) {
+  if (!p) return fail(MXFP4_ENULL, "%s is NULL", name);
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mxfp4_packed_bytes(int rows, int K) {
+  if (rows < 1 || K < 128 || K % 128 != 0) return 0;
+  return mx::packed_dims(rows, K).total_bytes();
+}
+
+int mxfp4_pack_b(const uint8_t* b_fp4, const uint8_t* b_scale, int N, int K, void* b_packed,
+                 size_t b_packed_bytes, void* stream) {
+  int rc;
+  if ((rc = check_stream_ptrs(b_fp4, "b_fp4")) || (rc = check_stream_ptrs(b_scale, "b_scale")) ||
+      (rc = check_stream_ptrs(b_packed, "b_packed")))
+    return rc;
+  if (N < 16 || N % 16 != 0) return fail(MXFP4_EINVAL, "N must be a positive multiple of 16 (got %d)", N);
+  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  if (!aligned(b_fp4, 16) || !aligned(b_packed, 16))
+    return fail(MXFP4_EINVAL, "b_fp4 and b_packed must be 16-byte aligned");
+  const size_t need = mxfp4_packed_bytes(N, K);
+  if (b_packed_bytes < need)
+    return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, need);
+  mx::launch_pack_b(b_fp4, b_scale, N, K, static_cast<uint8_t*>(b_packed),
+                    static_cast<hipStream_t>(stream));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pack_b launch");
+  return ok();
+}
+
+int mxfp4_quant_a(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
+                  uint8_t* out_scale, int ld_scale, void* stream) {
+  int rc;
+  if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(out_fp4, "out_fp4")) ||
+      (rc = check_stream_ptrs(out_scale, "out_scale")))
+    return rc;
+  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
+  if (ld_fp4 < K / 2 || ld_fp4 % 4 != 0)
+    return fail(MXFP4_EINVAL, "ld_fp4 must be >= K/2 and a multiple of 4 (got %d)", ld_fp4);
+  if (ld_scale < K / 32) return fail(MXFP4_EINVAL, "ld_scale must be >= K/32 (got %d)", ld_scale);
+  if (!aligned(a, 16) || !aligned(out_fp4, 4))
+    return fail(MXFP4_EINVAL, "a must be 16-byte and out_fp4 4-byte aligned");
+  if ((long long)M * K > (1LL << 40)) return fail(MXFP4_EINVAL, "M*K too large");
+  mx::launch_quant_linear(a, M, K, lda, out_fp4, ld_fp4, out_scale, ld_scale,
+                          static_cast<hipStream_t>(stream));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "quant_a launch");
+  return ok();
+}
+
+int mxfp4_quant_a_packed(const uint16_t* a, int M, int K, int lda, void* out_packed,
+                         size_t out_packed_bytes, void* stream) {
+  int rc;
+  if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(out_packed, "out_packed")))
+    return rc;
+  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
+  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
+  if (!aligned(a, 16) || !aligned(out_packed, 16))
+    return fail(MXFP4_EINVAL, "a and out_packed must be 16-byte aligned");
+  const size_t need = mxfp4_packed_bytes(M, K);
+  if (out_packed_bytes < need)
+    return fail(MXFP4_ESIZE, "out_packed holds %zu bytes, layout needs %zu", out_packed_bytes, need);
+  mx::launch_quant_packed(a, M, K, lda, static_cast<uint8_t*>(out_packed),
+                          static_cast<hipStream_t>(stream));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "quant_a_packed launch");
+  return ok();
+}
+
+int mxfp4_default_plan(int M, int N, int K, mxfp4_plan* plan) {
+  if (!plan) return fail(MXFP4_ENULL, "plan is NULL");
+  int rc = check_gemm_shape(M, N, K);
+  if (rc) return rc;
+  *plan = default_plan(M, N, K);
+  return ok();
+}
+
+int mxfp4_check_plan(const mxfp4_plan* plan, int M, int N, int K) {
+  if (!plan) return fail(MXFP4_ENULL, "plan is NULL");
+  int rc = check_gemm_shape(M, N, K);
+  if (rc) return rc;
+  if ((rc = check_plan(*plan, M, N, K, true))) return rc;
+  return ok();
+}
+
+size_t mxfp4_plan_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
+  if (!plan || check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
+  if (check_plan(*plan, M, N, K, true) != MXFP4_OK) return 0;
+  return plan_workspace(*plan, M, N, K, false);
+}
+
+size_t mxfp4_gemm_workspace_bytes(int M, int N, int K) {
+  if (check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
+  const mxfp4_plan p = default_plan(M, N, K);
+  return plan_workspace(p, M, N, K, false);
+}
+
+int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
+                  uint16_t* c, int ldc, int M, int N, int K, void* workspace,
+                  size_t workspace_bytes, const mxfp4_plan* plan, void* stream) {
+  int rc;
+  if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(b_packed, "b_packed")) ||
+      (rc = check_stream_ptrs(c, "c")))
+    return rc;
+  if ((rc = check_gemm_shape(M, N, K))) return rc;
+  if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
+  if (ldc < N) return fail(MXFP4_EINVAL, "ldc must be >= N (got %d)", ldc);
+  if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 2))
+    return fail(MXFP4_EINVAL, "a and b_packed must be 16-byte aligned, c 2-byte aligned");
+  const size_t bneed = mxfp4_packed_bytes(N, K);
+  if (b_packed_bytes < bneed)
+    return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
+  const mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
+  if ((rc = check_plan(p, M, N, K, true))) return rc;
+  const size_t wneed = plan_workspace(p, M, N, K, false);
+  if (wneed > 0) {
+    if (!workspace) return fail(MXFP4_ENULL, "workspace is NULL but the plan needs %zu bytes", wneed);
+    if (!aligned(workspace, 256)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wneed)
+      return fail(MXFP4_EWORKSPACE, "workspace holds %zu bytes, plan needs %zu", workspace_bytes, wneed);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const void* a_src = a;
+  if (p.mode == MXFP4_MODE_PREQUANT) {
+    mx::launch_quant_packed(a, M, K, lda, ws, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "quant_a_packed launch");
+    a_src = ws;
+    ws += round_up(mxfp4_packed_bytes(M, K), 256);
+  }
+  hipError_t e = mx::launch_gemm(to_internal(p), a_src, lda, static_cast<const uint8_t*>(b_packed), c,
+                                 ldc, M, N, K, reinterpret_cast<float*>(ws), st);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return ok();
+}
+
+int mxfp4_gemm(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
+               uint16_t* c, int ldc, int M, int N, int K, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return mxfp4_gemm_ex(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K, workspace,
+                       workspace_bytes, nullptr, stream);
+}
+
+int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void* b_packed,
+                        size_t b_packed_bytes, uint16_t* c, int ldc, int M, int N, int K,
+                        void* workspace, size_t workspace_bytes, const mxfp4_plan* plan,
+                        void* stream) {
+  int rc;
+  if ((rc = check_stream_ptrs(a_packed, "a_packed")) || (rc = check_stream_ptrs(b_packed, "b_packed")) ||
+      (rc = check_stream_ptrs(c, "c")))
+    return rc;
+  if ((rc = check_gemm_shape(M, N, K))) return rc;
+  if (ldc < N) return fail(MXFP4_EINVAL, "ldc must be >= N (got %d)", ldc);
+  if (!aligned(a_packed, 16) || !aligned(b_packed, 16) || !aligned(c, 2))
+    return fail(MXFP4_EINVAL, "a_packed and b_packed must be 16-byte aligned, c 2-byte aligned");
+  const size_t aneed = mxfp4_packed_bytes(M, K), bneed = mxfp4_packed_bytes(N, K);
+  if (a_packed_bytes < aneed)
+    return fail(MXFP4_ESIZE, "a_packed holds %zu bytes, layout needs %zu", a_packed_bytes, aneed);
+  if (b_packed_bytes < bneed)
+    return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
+  mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
+  p.mode = MXFP4_MODE_PREQUANT;
+  if ((rc = check_plan(p, M, N, K, false))) return rc;
+  const size_t wneed = plan_workspace(p, M, N, K, true);
+  if (wneed > 0) {
+    if (!workspace) return fail(MXFP4_ENULL, "workspace is NULL but the plan needs %zu bytes", wneed);
+    if (!aligned(workspace, 256)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wneed)
+      return fail(MXFP4_EWORKSPACE, "workspace holds %zu bytes, plan needs %zu", workspace_bytes, wneed);
+  }
+  hipError_t e = mx::launch_gemm(to_internal(p), a_packed, 0, static_cast<const uint8_t*>(b_packed), c,
+                                 ldc, M, N, K, static_cast<float*>(workspace),
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return ok();
+}
+
+const char* mxfp4_last_error(void) { return g_err; }
+
+const char* mxfp4_version(void) { return "mxfp4-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,448 @@
+// gemm.hip -- MXFP4 GEMM kernel (fused or pre-quantized A) and the split-K
+// reduce, for gfx950.
+//
+// Work decomposition (one workgroup):
+//   rows    [m0, m0 + 16*MBW)            MBW blocks of the MFMA's 16 rows
+//   columns wn wavefronts x NTW tiles of 16 columns
+//   K       wk wavefronts x KSW steps of 128, starting at step jw0
+// Each wavefront streams its own B tiles straight from HBM into registers
+// (16 bytes per lane per step, one coalesced 1 KiB block per load
+// instruction), issuing all of them before touching A so that the B
+// latency overlaps the A stage.  The workgroup's A rows for its K range are
+// staged once in LDS in the instruction's lane order -- quantized in the
+// kernel from bf16 (fused mode) or copied from the MX-packed A (prequant
+// mode) -- and every wavefront reads its A operand from there.  Partial tiles
+// of the wk wavefronts are summed in LDS in a fixed order; with split > 1 the
+// workgroup writes an fp32 partial and splitk_reduce_kernel sums them.
+#include <atomic>
+
+#include "mx_internal.hpp"
+
+namespace mx {
+
+struct GemmArgs {
+  const uint16_t* a;  // bf16 A [M][lda] (fused mode)
+  const uint8_t* ap;  // MX-packed A (prequant mode)
+  const uint8_t* bp;  // MX-packed B
+  uint16_t* c;        // bf16 C [M][ldc]
+  float* ws;          // fp32 partials [split][M][N]
+  int M, N, K, lda, ldc;
+  int MT, NT, KS, KG;
+  int wn, wk, split, mgroups, ngroups, kswg;
+  unsigned lds_asc_off, lds_red_off, lds_raw_off;
+};
+
+// LDS-direct loads: each active lane moves 16 (or 4) bytes from its own
+// global address to lds_base + lane*16 (or lane*4); lds_base must be the
+// same for the whole wavefront.
+__device__ inline void lds_load16(const void* gptr, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ inline void lds_load4(const void* gptr, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Scale dwords a wavefront's KSW consecutive steps can span.  Step ranges
+// start at multiples of KSW, so for KSW % 4 == 0 and KSW <= 2 they never
+// straddle more dwords than the step count needs.
+template <int KSW>
+struct ScaleSpan {
+  static constexpr int value = (KSW % 4 == 0) ? KSW / 4 : (KSW <= 2 ? 1 : (KSW + 6) / 4);
+};
+
+template <int MODE, int MBW, int NTW, int KSW>
+__global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int NSD = ScaleSpan<KSW>::value;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_n = wave % g.wn;
+  const int wave_k = wave / g.wn;
+  const int nthreads = blockDim.x;
+
+  int bid = blockIdx.x;
+  const int ng = bid % g.ngroups;
+  bid /= g.ngroups;
+  const int mg = bid % g.mgroups;
+  const int s = bid / g.mgroups;
+
+  const int m0 = mg * MBW * 16;
+  const int kswg = g.kswg;
+  const int jw0 = s * kswg;             // first K step of the workgroup
+  const int j0 = jw0 + wave_k * KSW;    // first K step of this wavefront
+  const int gw0 = jw0 >> 2;             // first scale dword of the workgroup
+  const int ngw = ((jw0 + kswg - 1) >> 2) - gw0 + 1;
+  const int nt_base = (ng * g.wn + wave_n) * NTW;
+
+  // ---- 1. issue every B load of this wavefront (clamped tile index keeps a
+  //         ragged last group in bounds; its results are never stored).
+  uint4 bq[NTW][KSW];
+  uint32_t bs[NTW][NSD];
+  const size_t b_sc_base = (size_t)g.NT * g.KS * kBlockBytes;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = min(nt_base + i, g.NT - 1);
+    const uint8_t* bt = g.bp + ((size_t)nt * g.KS + j0) * kBlockBytes + (size_t)lane * 16;
+#pragma unroll
+    for (int j = 0; j < KSW; ++j)
+      bq[i][j] = *reinterpret_cast<const uint4*>(bt + (size_t)j * kBlockBytes);
+    const uint8_t* bst = g.bp + b_sc_base + (size_t)nt * g.KG * 256 + (size_t)lane * 4;
+#pragma unroll
+    for (int d = 0; d < NSD; ++d) {
+      const int gi = min((j0 >> 2) + d, g.KG - 1);
+      bs[i][d] = *reinterpret_cast<const uint32_t*>(bst + (size_t)gi * 256);
+    }
+  }
+
+  // ---- 2. stage the workgroup's A rows for steps [jw0, jw0 + kswg) in LDS.
+  //         All of it moves by LDS-direct loads (global -> LDS without
+  //         registers, 1 KiB or 256 B per wavefront instruction), issued
+  //         right behind the B loads so every global load of the workgroup is
+  //         in flight at once; one wait then covers both.
+  const int nwaves = nthreads >> 6;
+  uint8_t* lds_a = smem;
+  uint8_t* lds_sc = smem + g.lds_asc_off;
+  uint8_t* lds_raw = smem + g.lds_raw_off;
+  const int rows_valid = min(MBW * 16, g.M - m0);
+  if constexpr (MODE == 1) {
+    // raw bf16 rows, row-major, kswg*256 bytes per row
+    const int chunks_per_row = kswg * 16;  // 16-byte chunks
+    const int n_chunks = rows_valid * chunks_per_row;
+    for (int ci = wave; ci * 64 < n_chunks; ci += nwaves) {
+      const int flat = ci * 64 + lane;
+      if (flat < n_chunks) {
+        const int r = flat / chunks_per_row;
+        const int c = flat - r * chunks_per_row;
+        lds_load16(g.a + (size_t)(m0 + r) * g.lda + (size_t)jw0 * kStep + (size_t)c * 8,
+                   lds_raw + (size_t)ci * 1024);
+      }
+    }
+  } else {
+    const PackedDims da = {g.MT, g.KS, g.KG};
+    const int mbv = min(MBW, g.MT - mg * MBW);
+    const int n_blocks = mbv * kswg;
+    for (int bi = wave; bi < n_blocks; bi += nwaves) {
+      const int b = bi / kswg;
+      const int jl = bi - b * kswg;
+      lds_load16(g.ap + da.data_off(mg * MBW + b, jw0 + jl, lane),
+                 lds_a + (size_t)(b * kswg + jl) * 1024);
+    }
+    const int n_sd = mbv * ngw;
+    for (int bi = wave; bi < n_sd; bi += nwaves) {
+      const int b = bi / ngw;
+      const int gl = bi - b * ngw;
+      lds_load4(g.ap + da.scale_off(mg * MBW + b, gw0 + gl, lane),
+                lds_sc + (size_t)(b * ngw + gl) * 256);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  if constexpr (MODE == 1) {
+    // Quantize the raw rows: one item = 8 consecutive bf16 (16 bytes), and
+    // the 4 items of an aligned quad of lanes form one 32-element group.
+    const int chunks_per_row = kswg * 16;
+    const int n_items = rows_valid * chunks_per_row;
+    int r = tid / chunks_per_row;
+    int c = tid - r * chunks_per_row;
+    for (int it = tid; it < n_items; it += nthreads) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + (size_t)it * 16);
+      const int jl = c >> 4;
+      const int kg = (c >> 2) & 3;
+      const int p = c & 3;
+      const int jj = jw0 + jl;
+      const uint32_t amax = quad_max(amax8_bits(v));
+      const uint32_t byte = scale_byte_from_amax(amax);
+      const uint32_t codes = encode8(v, inv_scale_from_byte(byte));
+      const int b = r >> 4;
+      const int ln = (r & 15) + 16 * kg;
+      *reinterpret_cast<uint32_t*>(lds_a + ((size_t)(b * kswg + jl) * 64 + ln) * 16 + 4 * p) =
+          codes;
+      if (p == 0)
+        lds_sc[((size_t)(b * ngw + (jj >> 2) - gw0) * 64 + ln) * 4 + (jj & 3)] = (uint8_t)byte;
+      c += nthreads;
+      while (c >= chunks_per_row) {
+        c -= chunks_per_row;
+        ++r;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 3. block-scaled FP4 products.  Rows >= M get scale byte 0 and are
+  //         never stored.
+  uint32_t rowmask[MBW];
+#pragma unroll
+  for (int b = 0; b < MBW; ++b) rowmask[b] = (m0 + b * 16 + (lane & 15)) < g.M ? 0xFFu : 0u;
+
+  f32x4 acc[MBW][NTW];
+#pragma unroll
+  for (int b = 0; b < MBW; ++b)
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A operands of one step for all MBW blocks; the next step's are read
+  // from LDS while the current step's products issue.
+  uint4 av[MBW];
+  uint32_t asd[MBW];
+  auto read_a = [&](int j, uint4 (&v)[MBW], uint32_t (&sd)[MBW]) {
+    const int jj = j0 + j;
+    const int jl = wave_k * KSW + j;
+#pragma unroll
+    for (int b = 0; b < MBW; ++b) {
+      v[b] = *reinterpret_cast<const uint4*>(lds_a + ((size_t)(b * kswg + jl) * 64 + lane) * 16);
+      sd[b] = *reinterpret_cast<const uint32_t*>(
+          lds_sc + ((size_t)(b * ngw + (jj >> 2) - gw0) * 64 + lane) * 4);
+    }
+  };
+  read_a(0, av, asd);
+
+#pragma unroll
+  for (int j = 0; j < KSW; ++j) {
+    uint4 avn[MBW];
+    uint32_t asdn[MBW];
+    if (j + 1 < KSW) read_a(j + 1, avn, asdn);
+    // keep the next step's LDS reads ahead of this step's products
+    __builtin_amdgcn_sched_barrier(0);
+    const int jj = j0 + j;
+    const int sh = (KSW % 4 == 0) ? 8 * (j & 3) : 8 * (jj & 3);
+    int bsc[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      uint32_t w;
+      if constexpr (KSW % 4 == 0 || KSW <= 2) {
+        w = bs[i][(KSW % 4 == 0) ? (j >> 2) : 0];
+      } else {
+        // runtime choice among NSD registers by selects (no indexed access,
+        // which would move the array to scratch memory)
+        const int dsel = (jj >> 2) - (j0 >> 2);
+        w = bs[i][0];
+#pragma unroll
+        for (int d = 1; d < NSD; ++d) w = (dsel == d) ? bs[i][d] : w;
+      }
+      bsc[i] = (int)((w >> sh) & 0xFFu);
+    }
+#pragma unroll
+    for (int b = 0; b < MBW; ++b) {
+      const int asc = (int)((asd[b] >> sh) & rowmask[b]);
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) acc[b][i] = mfma_fp4(av[b], bq[i][j], acc[b][i], asc, bsc[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < KSW) {
+#pragma unroll
+      for (int b = 0; b < MBW; ++b) {
+        av[b] = avn[b];
+        asd[b] = asdn[b];
+      }
+    }
+  }
+
+  // ---- 4. sum the wk wavefronts of one column group in LDS, in order.
+  if (g.wk > 1) {
+    float* red = reinterpret_cast<float*>(smem + g.lds_red_off);
+    constexpr int per_wave = MBW * NTW * 256;
+    if (wave_k > 0) {
+      float* dst = red + (size_t)((wave_k - 1) * g.wn + wave_n) * per_wave;
+#pragma unroll
+      for (int b = 0; b < MBW; ++b)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+          *reinterpret_cast<f32x4*>(dst + ((b * NTW + i) * 64 + lane) * 4) = acc[b][i];
+    }
+    __syncthreads();
+    if (wave_k > 0) return;
+    for (int kk = 1; kk < g.wk; ++kk) {
+      const float* src = red + (size_t)((kk - 1) * g.wn + wave_n) * per_wave;
+#pragma unroll
+      for (int b = 0; b < MBW; ++b)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+          acc[b][i] += *reinterpret_cast<const f32x4*>(src + ((b * NTW + i) * 64 + lane) * 4);
+    }
+  }
+
+  // ---- 5. store: bf16 (nearest even) or an fp32 partial.
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = nt_base + i;
+    if (nt >= g.NT) continue;
+    const int col = nt * 16 + (lane & 15);
+#pragma unroll
+    for (int b = 0; b < MBW; ++b) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
+        if (row >= g.M) continue;
+        if (g.split == 1)
+          g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[b][i][e]);
+        else
+          g.ws[((size_t)s * g.M + row) * g.N + col] = acc[b][i][e];
+      }
+    }
+  }
+}
+
+// Sum split fp32 partials [S][M][N] in order s = 0..S-1 and round to bf16.
+// One thread per 4 consecutive outputs (N % 16 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            uint16_t* __restrict__ c, int M,
+                                                            int N, int ldc, int S) {
+  const int n4 = N / 4;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)M * n4) return;
+  const int row = (int)(idx / n4);
+  const int col = (int)(idx % n4) * 4;
+  const size_t plane = (size_t)M * N;
+  const float* src = ws + (size_t)row * N + col;
+  float4 acc = *reinterpret_cast<const float4*>(src);
+  for (int k = 1; k < S; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * plane);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  uint16_t* dst = c + (size_t)row * ldc + col;
+  const uint16_t h0 = f32_to_bf16_rne(acc.x), h1 = f32_to_bf16_rne(acc.y);
+  const uint16_t h2 = f32_to_bf16_rne(acc.z), h3 = f32_to_bf16_rne(acc.w);
+  if ((((uintptr_t)dst) & 7) == 0) {
+    uint2 pk;
+    pk.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    pk.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+    *reinterpret_cast<uint2*>(dst) = pk;
+  } else {
+    dst[0] = h0;
+    dst[1] = h1;
+    dst[2] = h2;
+    dst[3] = h3;
+  }
+}
+
+// ------------------------------------------------------------ dispatch table
+
+#define MX_KSW_LIST(X, MODE, MBW, NTW) \
+  X(MODE, MBW, NTW, 1)                 \
+  X(MODE, MBW, NTW, 2)                 \
+  X(MODE, MBW, NTW, 3)                 \
+  X(MODE, MBW, NTW, 4)                 \
+  X(MODE, MBW, NTW, 6)                 \
+  X(MODE, MBW, NTW, 7)                 \
+  X(MODE, MBW, NTW, 8)                 \
+  X(MODE, MBW, NTW, 12)                \
+  X(MODE, MBW, NTW, 14)                \
+  X(MODE, MBW, NTW, 16)
+
+#define MX_NTW_LIST(X, MODE, MBW) \
+  MX_KSW_LIST(X, MODE, MBW, 1)    \
+  MX_KSW_LIST(X, MODE, MBW, 2)
+
+#define MX_MBW_LIST(X, MODE) \
+  MX_NTW_LIST(X, MODE, 1)    \
+  MX_NTW_LIST(X, MODE, 2)    \
+  MX_NTW_LIST(X, MODE, 4)
+
+#define MX_ALL_KERNELS(X) \
+  MX_MBW_LIST(X, 1)       \
+  MX_MBW_LIST(X, 2)
+
+struct KernelEntry {
+  int mode, mbw, ntw, ksw;
+  const void* fn;
+};
+
+#define MX_ENTRY(MODE, MBW, NTW, KSW) \
+  {MODE, MBW, NTW, KSW, reinterpret_cast<const void*>(&gemm_kernel<MODE, MBW, NTW, KSW>)},
+
+static const KernelEntry kKernels[] = {MX_ALL_KERNELS(MX_ENTRY)};
+constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
+static std::atomic<int> g_lds_attr_set[kNumKernels];
+
+static int find_kernel(int mode, int mbw, int ntw, int ksw) {
+  for (int i = 0; i < kNumKernels; ++i)
+    if (kKernels[i].mode == mode && kKernels[i].mbw == mbw && kKernels[i].ntw == ntw &&
+        kKernels[i].ksw == ksw)
+      return i;
+  return -1;
+}
+
+bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw) {
+  return find_kernel(mode, mbw, ntw, ksw) >= 0;
+}
+
+GemmGeom gemm_geometry(const Plan& p, int M, int N, int K) {
+  GemmGeom g;
+  g.MT = (M + 15) / 16;
+  g.NT = N / 16;
+  g.KS = K / kStep;
+  g.KG = (g.KS + 3) / 4;
+  g.mgroups = (g.MT + p.mbw - 1) / p.mbw;
+  const int cols_per_wg = p.wn * p.ntw;
+  g.ngroups = (g.NT + cols_per_wg - 1) / cols_per_wg;
+  g.kswg = p.wk * p.ksw;
+  g.ngw_max = (g.kswg % 4 == 0) ? g.kswg / 4 : (g.kswg + 6) / 4;
+  g.lds_a = (size_t)p.mbw * g.kswg * kBlockBytes;
+  g.lds_asc = (size_t)p.mbw * g.ngw_max * 256;
+  g.lds_red = p.wk > 1 ? (size_t)(p.wk - 1) * p.wn * p.mbw * p.ntw * 1024 : 0;
+  // raw bf16 rows of the fused stage; dead before the reduce area is used,
+  // so the two share one region
+  g.lds_raw = p.mode == 1 ? (size_t)p.mbw * 16 * g.kswg * 256 : 0;
+  g.lds_total = g.lds_a + g.lds_asc + (g.lds_red > g.lds_raw ? g.lds_red : g.lds_raw);
+  g.grid = (unsigned)((long long)g.mgroups * g.ngroups * p.split);
+  g.threads = p.wn * p.wk * 64;
+  return g;
+}
+
+hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_packed,
+                       uint16_t* c, int ldc, int M, int N, int K, float* ws,
+                       hipStream_t stream) {
+  const int ki = find_kernel(p.mode, p.mbw, p.ntw, p.ksw);
+  if (ki < 0) return hipErrorInvalidDeviceFunction;
+  const GemmGeom geo = gemm_geometry(p, M, N, K);
+  const void* fn = kKernels[ki].fn;
+  if (geo.lds_total > 64 * 1024 && !g_lds_attr_set[ki].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    g_lds_attr_set[ki].store(1, std::memory_order_release);
+  }
+  GemmArgs args;
+  args.a = p.mode == 1 ? static_cast<const uint16_t*>(a) : nullptr;
+  args.ap = p.mode == 2 ? static_cast<const uint8_t*>(a) : nullptr;
+  args.bp = b_packed;
+  args.c = c;
+  args.ws = ws;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.lda = lda;
+  args.ldc = ldc;
+  args.MT = geo.MT;
+  args.NT = geo.NT;
+  args.KS = geo.KS;
+  args.KG = geo.KG;
+  args.wn = p.wn;
+  args.wk = p.wk;
+  args.split = p.split;
+  args.mgroups = geo.mgroups;
+  args.ngroups = geo.ngroups;
+  args.kswg = geo.kswg;
+  args.lds_asc_off = (unsigned)geo.lds_a;
+  args.lds_red_off = (unsigned)(geo.lds_a + geo.lds_asc);
+  args.lds_raw_off = args.lds_red_off;
+  void* kargs[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3(geo.grid), dim3(geo.threads), kargs,
+                                 (unsigned)geo.lds_total, stream);
+  if (e != hipSuccess) return e;
+  if (p.split > 1) {
+    const long long n = (long long)M * (N / 4);
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, M, N, ldc,
+                       p.split);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace mx

@@ -1,0 +1,130 @@
+// mx_device.hpp -- gfx950 device helpers shared by the MXFP4 kernels:
+// MX-packed layout offsets, the group scale rule, the e2m1 encoder and the
+// block-scaled FP4 matrix instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 32;        // K-elements per e8m0 scale
+constexpr int kStep = 128;        // K-elements per matrix instruction
+constexpr int kTileRows = 16;     // rows per packed tile
+constexpr int kBlockBytes = 1024; // one (tile, step) data block: 64 lanes x 16 B
+
+// ---------------------------------------------------------------- layout
+// MX-packed layout of R rows x K columns (see mxfp4.h for the closed form).
+struct PackedDims {
+  int RT;  // row tiles
+  int KS;  // 128-K steps
+  int KG;  // scale dwords per (tile, lane): ceil(KS/4)
+  __host__ __device__ size_t data_bytes() const { return (size_t)RT * KS * kBlockBytes; }
+  __host__ __device__ size_t total_bytes() const { return data_bytes() + (size_t)RT * KG * 256; }
+  __host__ __device__ size_t data_off(int t, int j, int lane) const {
+    return (((size_t)t * KS + j) * 64 + lane) * 16;
+  }
+  __host__ __device__ size_t scale_off(int t, int g, int lane) const {
+    return data_bytes() + (((size_t)t * KG + g) * 64 + lane) * 4;
+  }
+};
+
+__host__ __device__ inline PackedDims packed_dims(int rows, int K) {
+  PackedDims d;
+  d.RT = (rows + kTileRows - 1) / kTileRows;
+  d.KS = K / kStep;
+  d.KG = (d.KS + 3) / 4;
+  return d;
+}
+
+// ------------------------------------------------------------- bf16 bits
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Largest |bf16| of the 8 values in v, as a bf16 magnitude bit pattern.
+// Magnitude bit patterns of finite values order like the values themselves.
+__device__ inline uint32_t amax8_bits(uint4 v) {
+  uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+  uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+  uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+  uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+  return max(max(m0, m1), max(m2, m3));
+}
+
+// Max over the 4 lanes of an aligned quad (lanes 4q..4q+3), by two DPP
+// quad permutations.  All four lanes must be active.
+__device__ inline uint32_t quad_max(uint32_t x) {
+  uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+  x = max(x, y);
+  y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+  return max(x, y);
+}
+
+// e8m0 scale byte from the group maximum (bf16 magnitude bits): add 2^21 to
+// the fp32 pattern (round the maximum up to a power of two when its
+// significand is at least 1.75), take the biased exponent e; the unbiased
+// scale exponent is e - 127 - 2, clamped to [-127, 127]; the byte is that
+// plus 127, i.e. max(e - 2, 0).  (Rule of submission 752099 `_bf16_to_fp4_hw`.)
+__device__ inline uint32_t scale_byte_from_amax(uint32_t amax_bf16_bits) {
+  uint32_t e = (((amax_bf16_bits << 16) + 0x00200000u) >> 23) & 0xFFu;
+  return e > 2u ? e - 2u : 0u;
+}
+
+// 2^-(byte - 127) as an fp32 number: exponent field 254 - byte, normal for
+// every byte a finite input can produce (0..253).
+__device__ inline float inv_scale_from_byte(uint32_t byte) {
+  return __uint_as_float((254u - byte) << 23);
+}
+
+// e2m1 code (bits 0..2) of a non-negative, already scaled magnitude q:
+// nearest grid value, ties to even, saturating at 6.  The grid spacing is
+// 0.5 below 2, 1 in [2, 4) and 2 in [4, 6); rounding in units of the
+// spacing with the hardware round-half-even and adding the index of the
+// binade's first code gives the code directly.
+__device__ inline uint32_t e2m1_mag_code(float q) {
+  float mul = q < 2.0f ? 2.0f : (q < 4.0f ? 1.0f : 0.5f);
+  float off = q < 2.0f ? 0.0f : (q < 4.0f ? 2.0f : 4.0f);
+  float c = fminf(__builtin_rintf(q * mul) + off, 7.0f);
+  return (uint32_t)c;
+}
+
+// Encode 8 bf16 values (v, in memory order) under one inverse scale into 8
+// e2m1 codes, element i in nibble i of the result (so byte j holds elements
+// 2j and 2j+1, even element in the low nibble).  The sign of each input goes
+// to bit 3 of its code, including values that round to zero.
+__device__ inline uint32_t encode8(uint4 v, float inv) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = e2m1_mag_code(fabsf(bf16_lo(w[i])) * inv) | ((w[i] >> 12) & 8u);
+    uint32_t hi = e2m1_mag_code(fabsf(bf16_hi(w[i])) * inv) | ((w[i] >> 28) & 8u);
+    out |= (lo | (hi << 4)) << (8 * i);
+  }
+  return out;
+}
+
+// ------------------------------------------------------ matrix instruction
+// One gfx950 block-scaled 16x16x128 FP4 x FP4 product-accumulate.
+//   a: this lane's 32 A codes (row L%16, K-group L/16), 16 bytes;
+//   b: this lane's 32 B codes (column L%16, K-group L/16), 16 bytes;
+//   sa, sb: this lane's e8m0 scale bytes (low byte used);
+//   acc: 4 fp32 of C, rows 4*(L/16)+e, column L%16.
+__device__ inline f32x4 mfma_fp4(uint4 a, uint4 b, f32x4 acc, int sa, int sb) {
+  i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  i32x8 b8 = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // format 4 = e2m1 for both operands; byte 0 of each scale register.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc, 4, 4, 0, sa, 0, sb);
+}
+
+}  // namespace mx

@@ -1,0 +1,59 @@
+// mx_internal.hpp -- declarations shared between the kernel files and the
+// C-ABI layer (api.cpp).  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_device.hpp"
+
+namespace mx {
+
+// Tiling of one GEMM call (mirrors the public mxfp4_plan).
+struct Plan {
+  int mode;      // 1 fused, 2 prequant
+  int mbw;       // 16-row A blocks per workgroup
+  int ntw;       // 16-column B tiles per wavefront
+  int wn;        // wavefronts along N
+  int wk;        // wavefronts along K
+  int ksw;       // 128-K steps per wavefront
+  int split;     // workgroups along K
+};
+
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxThreads = 512;
+
+// Launch geometry derived from a plan and a shape.
+struct GemmGeom {
+  int MT, NT, KS, KG;
+  int mgroups, ngroups;
+  int kswg;        // steps per workgroup = wk * ksw
+  int ngw_max;     // scale dwords per (block, lane) the workgroup may span
+  size_t lds_a;    // bytes of A data in LDS
+  size_t lds_asc;  // bytes of A scales in LDS
+  size_t lds_red;  // bytes of the in-block reduce area
+  size_t lds_raw;  // bytes of raw bf16 A rows (fused mode)
+  size_t lds_total;
+  unsigned grid;
+  int threads;
+};
+
+GemmGeom gemm_geometry(const Plan& p, int M, int N, int K);
+
+// True when a kernel for (mode, mbw, ntw, ksw) is compiled in.
+bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw);
+
+// Enqueue the GEMM kernel (and the split-K reduce when p.split > 1).
+//   a: bf16 A (fused) or MX-packed A (prequant); ws: fp32 partials.
+hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_packed,
+                       uint16_t* c, int ldc, int M, int N, int K, float* ws,
+                       hipStream_t stream);
+
+void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
+                         uint8_t* out_scale, int ld_scale, hipStream_t stream);
+void launch_quant_packed(const uint16_t* a, int M, int K, int lda, uint8_t* out,
+                         hipStream_t stream);
+void launch_pack_b(const uint8_t* b_fp4, const uint8_t* b_scale, int N, int K, uint8_t* out,
+                   hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,184 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 GEMM library, libmxfp4.so.
+ *
+ * The library computes C[M,N] = A[M,K] . B[N,K]^T with bf16 output, where A
+ * arrives as bf16 and is quantized on the fly to MXFP4, and B arrives already
+ * quantized.  MXFP4 here means: one e8m0 scale byte per 32 consecutive
+ * K-elements of a row, and one 4-bit e2m1 code per element, two codes per
+ * byte (element 2j in the low nibble of byte j).  Sources, all kernelindex.com
+ * "kernelbot amd-mxfp4-mm" submissions:
+ *   - scale rule: submission 752099 `_bf16_to_fp4_hw`, submission 754549
+ *     `_quantize_mxfp4`, submission 739530 `hw_quant32` (zero group);
+ *   - element rounding (nearest, ties to even, saturate at 6, sign on bit 3)
+ *     and nibble order: submission 694791 `_mxfp4_quant_tile`;
+ *   - block-scaled dot with fp32 accumulation: submission 752099
+ *     `_quant_gemm_fused_launcher` (`tl.dot_scaled`), submission 739530
+ *     `fgemm_pq` (the gfx950 scaled FP4 matrix instruction);
+ *   - split-K with an fp32 workspace and a reduce pass: submission 739530
+ *     `_gemm_k` / `_reduce_k`, submission 752099 `_splitk_sum_launcher`.
+ *
+ * Conventions for every call below:
+ *   - pointers named a, b_*, c, workspace, *_packed and out_* are DEVICE
+ *     pointers; the plan pointer is a HOST pointer;
+ *   - `stream` is a hipStream_t (NULL = the default stream); all device work
+ *     is enqueued asynchronously on it and nothing is synchronised;
+ *   - the library never allocates or frees device memory: the caller owns
+ *     every buffer, and the size queries say how large each must be;
+ *   - return value 0 is success; a negative value is one of MXFP4_E* below.
+ *     On any error other than MXFP4_EHIP nothing has been enqueued.  The
+ *     text of the last error of the calling thread is mxfp4_last_error();
+ *   - calls are thread-safe; the library holds no per-call device state.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP4_OK 0
+#define MXFP4_EINVAL (-1)     /* bad shape, stride or alignment */
+#define MXFP4_ENULL (-2)      /* a required pointer is NULL */
+#define MXFP4_EWORKSPACE (-3) /* workspace smaller than the plan needs */
+#define MXFP4_ESIZE (-4)      /* a packed buffer is smaller than its layout */
+#define MXFP4_ENOTSUP (-5)    /* plan fields not available in this build */
+#define MXFP4_EHIP (-6)       /* the HIP runtime reported a launch error */
+
+/* ------------------------------------------------------------------------
+ * Packed operand layout ("MX-packed").
+ *
+ * Both the pre-packed B and the pre-quantized A use one layout, laid out in
+ * the lane order of the gfx950 block-scaled 16x16x128 FP4 matrix instruction
+ * (lane L holds row L%16 and the 32-element K-group L/16 of a 128-K step).
+ * For a matrix of R rows and K columns (K % 128 == 0):
+ *     RT = ceil(R/16) row tiles, KS = K/128 steps, KG = ceil(KS/4),
+ *     data bytes  D = RT*KS*1024,  total bytes = D + RT*KG*256.
+ *   data:  byte ((t*KS + j)*64 + L)*16 + i  holds linear fp4x2 byte
+ *          (64*j + 16*(L/16) + i) of row 16*t + L%16,  i in [0,16);
+ *   scale: byte D + ((t*KG + g)*64 + L)*4 + s  holds the e8m0 scale of row
+ *          16*t + L%16, K-group 4*(4*g + s) + L/16, for step 4*g+s < KS;
+ *          bytes for steps >= KS hold 127.
+ * Rows >= R (padding of the last tile) hold code 0 and scale 127.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the MX-packed layout for `rows` rows of K columns; 0 when
+ * rows < 1 or K is not a positive multiple of 128. */
+size_t mxfp4_packed_bytes(int rows, int K);
+
+/* One-time repack of a quantized B into the MX-packed layout.
+ *   b_fp4   [N][K/2]  fp4x2, row-major, contiguous (16-byte aligned);
+ *   b_scale [N][K/32] e8m0,  row-major, contiguous;
+ *   b_packed  output, mxfp4_packed_bytes(N, K) bytes, 16-byte aligned.
+ * Requires N % 16 == 0, N >= 16, K % 128 == 0, K >= 128.  This is a byte
+ * permutation only (no arithmetic).  Errors: ENULL, EINVAL, ESIZE, EHIP. */
+int mxfp4_pack_b(const uint8_t *b_fp4, const uint8_t *b_scale, int N, int K, void *b_packed,
+                 size_t b_packed_bytes, void *stream);
+
+/* Quantize bf16 rows to MXFP4 in the linear layout.
+ *   a        [M][lda] bf16 bit patterns (uint16), 16-byte aligned, lda % 8 == 0;
+ *   out_fp4  [M][ld_fp4] bytes, row m gets K/2 bytes, ld_fp4 >= K/2, ld_fp4 % 4 == 0,
+ *            4-byte aligned;
+ *   out_scale [M][ld_scale] bytes, row m gets K/32 bytes, ld_scale >= K/32.
+ * Requires M >= 1, K >= 32, K % 32 == 0, lda >= K.  The group scale is the
+ * rule of submission 752099 `_bf16_to_fp4_hw`; elements round to nearest
+ * e2m1 with ties to even and saturate at 6 (submission 694791).  Results are
+ * bit-exact to that definition.  Errors: ENULL, EINVAL, EHIP. */
+int mxfp4_quant_a(const uint16_t *a, int M, int K, int lda, uint8_t *out_fp4, int ld_fp4,
+                  uint8_t *out_scale, int ld_scale, void *stream);
+
+/* Quantize bf16 rows straight into the MX-packed layout (the layout the
+ * GEMM reads), padding rows included.
+ *   a  as for mxfp4_quant_a;  out_packed  mxfp4_packed_bytes(M, K) bytes,
+ *   16-byte aligned.  Requires K % 128 == 0.  Errors: ENULL, EINVAL, ESIZE, EHIP. */
+int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_packed,
+                         size_t out_packed_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * GEMM plans.
+ *
+ * A plan fixes how one call is split over the GPU.  The grid has
+ * ceil(ceil(M/16)/m_blocks) * ceil((N/16)/(waves_n*n_tiles_per_wave)) *
+ * split_k workgroups of waves_n*waves_k wavefronts; each wavefront owns
+ * n_tiles_per_wave 16-column tiles of B, m_blocks 16-row blocks of A, and
+ * k_steps_per_wave 128-element K-steps.  The K steps must be covered
+ * exactly: split_k * waves_k * k_steps_per_wave == K/128.  waves_k > 1 sums
+ * the wavefronts' partial tiles in LDS (fixed order); split_k > 1 writes fp32
+ * partials [split_k][M][N] to the workspace and a reduce pass sums them in
+ * order s = 0..split_k-1 and rounds to bf16 (nearest even).
+ *
+ * mode FUSED quantizes the workgroup's A rows inside the GEMM kernel; mode
+ * PREQUANT first runs the quantizer once into the workspace (MX-packed) and
+ * the GEMM kernel reads fp4 A.
+ * ---------------------------------------------------------------------- */
+#define MXFP4_MODE_FUSED 1
+#define MXFP4_MODE_PREQUANT 2
+
+typedef struct mxfp4_plan {
+    int mode;             /* MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT */
+    int m_blocks;         /* 16-row blocks of A per workgroup: 1, 2 or 4 */
+    int n_tiles_per_wave; /* 16-column tiles of B per wavefront: 1 or 2 */
+    int waves_n;          /* wavefronts along N per workgroup */
+    int waves_k;          /* wavefronts along K per workgroup (in-LDS reduce) */
+    int k_steps_per_wave; /* 128-K steps per wavefront: 1,2,3,4,6,7,8,12,14,16 */
+    int split_k;          /* workgroups along K (fp32 workspace + reduce) */
+} mxfp4_plan;
+
+/* The plan mxfp4_gemm uses for a shape (a per-shape table for the tuned
+ * shapes, a heuristic otherwise).  Errors: ENULL, EINVAL. */
+int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
+
+/* MXFP4_OK when `plan` is valid for the shape and compiled in this build;
+ * otherwise the status mxfp4_gemm_ex would return for it (EINVAL, ENOTSUP,
+ * ENULL), with the reason in mxfp4_last_error(). */
+int mxfp4_check_plan(const mxfp4_plan *plan, int M, int N, int K);
+
+/* Workspace bytes a plan needs for a shape: the MX-packed A in PREQUANT
+ * mode (rounded up to 256 bytes) plus split_k*M*N*4 bytes of fp32 partials
+ * when split_k > 1.  0 when none is needed or the plan is invalid. */
+size_t mxfp4_plan_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
+
+/* Workspace bytes of the default plan. */
+size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
+
+/* C = A . B^T with the default plan.
+ *   a         [M][lda] bf16, 16-byte aligned, lda % 8 == 0, lda >= K;
+ *   b_packed  MX-packed B of N rows (from mxfp4_pack_b), b_packed_bytes >=
+ *             mxfp4_packed_bytes(N, K);
+ *   c         [M][ldc] bf16 output, ldc >= N; only the M x N block is written;
+ *   workspace device scratch of at least mxfp4_gemm_workspace_bytes(M,N,K)
+ *             bytes, 256-byte aligned (may be NULL when that is 0).
+ * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ * Inputs are finite.  Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
+int mxfp4_gemm(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
+               uint16_t *c, int ldc, int M, int N, int K, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* As mxfp4_gemm with an explicit plan (NULL = default plan). */
+int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
+                  uint16_t *c, int ldc, int M, int N, int K, void *workspace,
+                  size_t workspace_bytes, const mxfp4_plan *plan, void *stream);
+
+/* GEMM on an A that is already MX-packed (from mxfp4_quant_a_packed), for
+ * callers that quantize one activation once and use it against several
+ * weights.  The plan's mode is ignored (the kernel reads fp4 A); NULL plan =
+ * the default plan's tiling.  Workspace: split_k*M*N*4 bytes when split_k > 1.
+ * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
+int mxfp4_gemm_prequant(const void *a_packed, size_t a_packed_bytes, const void *b_packed,
+                        size_t b_packed_bytes, uint16_t *c, int ldc, int M, int N, int K,
+                        void *workspace, size_t workspace_bytes, const mxfp4_plan *plan,
+                        void *stream);
+
+/* Text of the last error returned on the calling thread ("" if none). */
+const char *mxfp4_last_error(void);
+
+/* Library version string. */
+const char *mxfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mxfp4.h declares, and its host-side checks reject bad arguments
+before anything is enqueued (every case below fails a check that precedes
+all HIP calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_quant_amd as mx
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+EINVAL, ENULL, EWORKSPACE, ESIZE, ENOTSUP = -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.library_path()):
+        from block_scaled_precision_quant_amd import _build
+        _build.build()
+    return mx.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(mx._SIGNATURES), "binding and header disagree"
+
+
+def test_version(lib):
+    assert mx.version().startswith("mxfp4-gfx950")
+
+
+def test_packed_bytes_closed_form(lib):
+    for rows, K in [(16, 128), (4, 512), (2880, 512), (2112, 7168), (17, 640), (256, 1536)]:
+        RT, KS = -(-rows // 16), K // 128
+        KG = -(-KS // 4)
+        assert mx.packed_bytes(rows, K) == RT * KS * 1024 + RT * KG * 256
+    # B's layout is exactly N*K/2 + N*K/32 bytes when K % 512 == 0
+    assert mx.packed_bytes(2880, 512) == 2880 * 256 + 2880 * 16
+    assert mx.packed_bytes(0, 512) == 0 and mx.packed_bytes(16, 100) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails first
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    f = lib.mxfp4_gemm
+    nb = mx.packed_bytes(32, 512)
+    assert f(None, 512, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == ENULL
+    assert f(FAKE, 512, None, nb, FAKE, 32, 4, 32, 512, None, 0, None) == ENULL
+    assert f(FAKE, 512, FAKE, nb, None, 32, 4, 32, 512, None, 0, None) == ENULL
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 0, 32, 512, None, 0, None) == EINVAL  # M
+    assert f(FAKE, 512, FAKE, nb, FAKE, 40, 4, 40, 512, None, 0, None) == EINVAL  # N % 16
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 32, 500, None, 0, None) == EINVAL  # K % 128
+    assert f(FAKE, 256, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda < K
+    assert f(FAKE, 516, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda % 8
+    assert f(FAKE, 512, FAKE, nb, FAKE, 16, 4, 32, 512, None, 0, None) == EINVAL  # ldc < N
+    assert "ldc" in mx.load().mxfp4_last_error().decode()
+    odd = ctypes.c_void_p(0x10008)
+    assert f(odd, 512, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # alignment
+    assert f(FAKE, 512, FAKE, nb - 1, FAKE, 32, 4, 32, 512, None, 0, None) == ESIZE
+
+
+def test_gemm_rejects_bad_plans_and_workspace(lib):
+    f = lib.mxfp4_gemm_ex
+    M, N, K = 64, 256, 2048
+    nb = mx.packed_bytes(N, K)
+
+    def call(plan, ws=None, wsb=0):
+        cp = plan._c()
+        return f(FAKE, K, FAKE, nb, FAKE, N, M, N, K, ws, wsb, ctypes.byref(cp), None)
+
+    good = mx.Plan(mx.MODE_PREQUANT, 4, 1, 2, 1, 16, 1)
+    need = mx.workspace_bytes(M, N, K, good)
+    assert need == (mx.packed_bytes(M, K) + 255) // 256 * 256
+    assert call(good, None, 0) == ENULL                     # workspace required
+    assert call(good, FAKE, need - 1) == EWORKSPACE
+    assert call(good, ctypes.c_void_p(0x10010), need) == EINVAL  # 256-byte alignment
+    assert lib.mxfp4_check_plan(ctypes.byref(good._c()), M, N, K) == 0
+    assert call(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
+    assert call(mx.Plan(1, 3, 1, 2, 1, 16, 1)) == ENOTSUP      # m_blocks
+    assert call(mx.Plan(1, 4, 1, 2, 1, 5, 1)) == ENOTSUP       # k_steps_per_wave
+    assert call(mx.Plan(1, 4, 1, 2, 1, 8, 1)) == EINVAL        # covers 8 of 16 steps
+    assert call(mx.Plan(1, 1, 1, 8, 2, 8, 1)) == EINVAL        # 16 wavefronts
+    # fused stage of 64 rows x 2048 K in LDS does not fit
+    assert call(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 1, 16, 1)) == EINVAL
+    assert "LDS" in mx.load().mxfp4_last_error().decode()
+    split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4)
+    assert mx.workspace_bytes(M, N, K, split) == 4 * M * N * 4
+    assert call(split, FAKE, 4 * M * N * 4 - 4) == EWORKSPACE
+
+
+def test_quant_and_pack_reject_bad_arguments(lib):
+    q = lib.mxfp4_quant_a
+    assert q(None, 4, 512, 512, FAKE, 256, FAKE, 16, None) == ENULL
+    assert q(FAKE, 0, 512, 512, FAKE, 256, FAKE, 16, None) == EINVAL
+    assert q(FAKE, 4, 48, 48, FAKE, 24, FAKE, 2, None) == EINVAL      # K % 32
+    assert q(FAKE, 4, 512, 512, FAKE, 128, FAKE, 16, None) == EINVAL  # ld_fp4 < K/2
+    assert q(FAKE, 4, 512, 512, FAKE, 256, FAKE, 8, None) == EINVAL   # ld_scale < K/32
+    qp = lib.mxfp4_quant_a_packed
+    assert qp(FAKE, 4, 512, 512, FAKE, mx.packed_bytes(4, 512) - 1, None) == ESIZE
+    assert qp(FAKE, 4, 96, 96, FAKE, 1 << 20, None) == EINVAL         # K % 128
+    pb = lib.mxfp4_pack_b
+    assert pb(FAKE, FAKE, 24, 512, FAKE, 1 << 20, None) == EINVAL     # N % 16
+    assert pb(FAKE, FAKE, 32, 512, FAKE, mx.packed_bytes(32, 512) - 1, None) == ESIZE
+    assert pb(FAKE, None, 32, 512, FAKE, 1 << 20, None) == ENULL
+
+
+def test_default_plans_are_valid(lib):
+    from block_scaled_precision_quant_amd import inputs
+    shapes = [(w.M, w.N, w.K) for w in inputs.WORKLOADS.values()]
+    shapes += [(8, 2112, 7168), (16, 3072, 1536), (64, 3072, 1536), (256, 2880, 512),
+               (1, 16, 128), (100, 1008, 1152), (33, 528, 640)]
+    for M, N, K in shapes:
+        p = mx.default_plan(M, N, K)
+        mx.check_plan(p, M, N, K)
+        assert p.split_k * p.waves_k * p.k_steps_per_wave == K // 128, (M, N, K, p)
+        # a valid plan has a well-defined workspace size (0 only if none needed)
+        ws = mx.workspace_bytes(M, N, K, p)
+        if p.mode == mx.MODE_PREQUANT or p.split_k > 1:
+            assert ws > 0
+        assert ws == mx.workspace_bytes(M, N, K)

@@ -1,0 +1,174 @@
+"""GPU GEMM parity against the CPU oracle, through the C ABI.
+
+Bar: |C_gpu - C_ref| <= 1e-2*|C_ref| + 1e-2 elementwise, C_ref the oracle's
+fp32 sum over the oracle's own quantization of A and B.  B goes to the GPU
+as the oracle's fp4/e8m0 bytes and is repacked by mxfp4_pack_b.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_precision_quant_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import block_scaled_precision_quant_amd as mx  # noqa: E402
+from gpu_util import assert_close_to_oracle, bf16_out_to_f32, to_dev_bf16, to_dev_u8  # noqa: E402
+
+F, P = mx.MODE_FUSED, mx.MODE_PREQUANT
+
+_REF_CACHE = {}
+
+
+def reference(name_or_shape, seed=None):
+    key = (name_or_shape, seed)
+    if key not in _REF_CACHE:
+        if isinstance(name_or_shape, str):
+            a, b = inputs.make(name_or_shape, seed=seed)
+        else:
+            M, N, K, sd = name_or_shape
+            a, b = inputs.make_shape(M, N, K, seed=sd)
+        ref = oracle.reference(a, b)
+        ref["a_bits"] = a
+        _REF_CACHE[key] = ref
+        if len(_REF_CACHE) > 4:
+            _REF_CACHE.pop(next(iter(_REF_CACHE)))
+    return _REF_CACHE[key]
+
+
+def run_gemm(ref, plan=None, poison=True):
+    a = to_dev_bf16(ref["a_bits"])
+    M, K = ref["a_bits"].shape
+    N = ref["bq"].shape[0]
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=a.device)
+    ws = None
+    nws = mx.workspace_bytes(M, N, K, plan)
+    if nws:
+        ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=a.device)  # NaN poison
+    mx.gemm(a, b_packed, N, out=c, workspace=ws, plan=plan)
+    torch.cuda.synchronize()
+    return bf16_out_to_f32(c)
+
+
+@pytest.mark.parametrize("name", inputs.ORDER)
+def test_workload_default_plan(name):
+    print("case", name, mx.default_plan(*[inputs.WORKLOADS[name].__dict__[k] for k in "MNK"]),
+          flush=True)
+    ref = reference(name)
+    assert_close_to_oracle(run_gemm(ref), ref["c32"], name)
+
+
+@pytest.mark.parametrize("name", ["m4_n2880_k512", "m16_n2112_k7168"])
+def test_workload_fresh_seed(name):
+    seed = inputs.WORKLOADS[name].seed + 1000
+    ref = reference(name, seed=seed)
+    assert_close_to_oracle(run_gemm(ref), ref["c32"], name + " fresh seed")
+
+
+PLANS = {
+    "m4_n2880_k512": [mx.Plan(F, 1, 1, 1, 1, 4, 1), mx.Plan(F, 1, 1, 4, 1, 4, 1),
+                      mx.Plan(F, 1, 1, 1, 4, 1, 1), mx.Plan(F, 1, 2, 2, 2, 2, 1),
+                      mx.Plan(P, 1, 1, 2, 1, 4, 1), mx.Plan(F, 1, 1, 2, 1, 2, 2),
+                      mx.Plan(P, 1, 2, 1, 1, 1, 4)],
+    "m32_n2880_k512": [mx.Plan(F, 2, 1, 2, 1, 4, 1), mx.Plan(F, 2, 2, 4, 1, 4, 1),
+                       mx.Plan(F, 1, 1, 2, 2, 2, 1), mx.Plan(P, 2, 1, 4, 1, 4, 1),
+                       mx.Plan(P, 1, 1, 2, 1, 2, 2)],
+    "m16_n2112_k7168": [mx.Plan(P, 1, 1, 1, 2, 7, 4), mx.Plan(F, 1, 1, 1, 2, 7, 4),
+                        mx.Plan(F, 1, 1, 2, 1, 14, 4), mx.Plan(P, 1, 1, 1, 1, 8, 7),
+                        mx.Plan(P, 1, 2, 2, 2, 14, 2), mx.Plan(P, 1, 1, 1, 4, 14, 1),
+                        mx.Plan(P, 1, 1, 1, 8, 7, 1)],
+    "m64_n7168_k2048": [mx.Plan(P, 4, 1, 2, 1, 16, 1), mx.Plan(F, 4, 1, 2, 1, 4, 4),
+                        mx.Plan(P, 2, 2, 2, 2, 8, 1), mx.Plan(P, 4, 1, 4, 1, 8, 2),
+                        mx.Plan(F, 2, 1, 4, 1, 8, 2)],
+    "m256_n3072_k1536": [mx.Plan(P, 4, 1, 4, 1, 12, 1), mx.Plan(P, 4, 2, 2, 1, 12, 1),
+                         mx.Plan(P, 2, 1, 4, 2, 6, 1), mx.Plan(P, 4, 1, 2, 1, 3, 4),
+                         mx.Plan(F, 4, 1, 2, 1, 6, 2)],
+}
+
+
+@pytest.mark.parametrize("name,plan", [(n, p) for n, ps in PLANS.items() for p in ps],
+                         ids=lambda x: str(x) if isinstance(x, str) else
+                         "m%d_mb%d_nt%d_wn%d_wk%d_ks%d_s%d" % (x.mode, x.m_blocks,
+                                                             x.n_tiles_per_wave, x.waves_n,
+                                                             x.waves_k, x.k_steps_per_wave,
+                                                             x.split_k))
+def test_workload_plan_override(name, plan):
+    w = inputs.WORKLOADS[name]
+    print("case", name, plan, flush=True)
+    mx.check_plan(plan, w.M, w.N, w.K)
+    ref = reference(name)
+    assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "%s %s" % (name, plan))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 48, 256), (17, 80, 384), (33, 144, 640),
+                                   (100, 1008, 1152), (63, 272, 896), (2, 16, 7168)])
+def test_ragged_shapes_default_plan(M, N, K):
+    print("case", M, N, K, mx.default_plan(M, N, K), flush=True)
+    ref = reference((M, N, K, M * 7 + N))
+    assert_close_to_oracle(run_gemm(ref), ref["c32"], "%dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K,plan", [
+    (7, 80, 512, mx.Plan(F, 1, 2, 2, 1, 4, 1)),   # ragged N group (5 tiles over 4)
+    (40, 48, 384, mx.Plan(F, 2, 1, 2, 1, 3, 1)),  # ragged M block, KSW=3 scale span
+    (40, 48, 768, mx.Plan(P, 4, 1, 1, 1, 6, 1)),
+    (20, 64, 1792, mx.Plan(F, 2, 1, 1, 2, 7, 1)),
+    (20, 64, 1792, mx.Plan(P, 1, 1, 4, 1, 14, 1)),
+])
+def test_ragged_shapes_plans(M, N, K, plan):
+    print("case", M, N, K, plan, flush=True)
+    ref = reference((M, N, K, 99 + M))
+    assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "%dx%dx%d %s" % (M, N, K, plan))
+
+
+def test_lane_map_one_hot():
+    """One-hot A rows against structured B pin rows, columns and K groups."""
+    M, N, K = 16, 32, 256
+    a = np.zeros((M, K), dtype=np.uint16)
+    one = np.uint16(0x3F80)
+    ks = [(m * 37 + 5) % K for m in range(M)]
+    for m in range(M):
+        a[m, ks[m]] = one
+    _, b = inputs.make_shape(M, N, K, seed=3)
+    ref = oracle.reference(a, b)
+    ref["a_bits"] = a
+    got = run_gemm(ref, mx.Plan(F, 1, 1, 2, 1, 2, 1))
+    for m in range(M):
+        np.testing.assert_array_equal(got[m], inputs.bf16_bits_to_f32(
+            inputs.f32_to_bf16_bits(ref["bd"][:, ks[m]].astype(np.float32))))
+
+
+def test_bitwise_repeatable():
+    ref = reference("m16_n2112_k7168")
+    p = mx.default_plan(16, 2112, 7168)
+    c1 = run_gemm(ref, p)
+    c2 = run_gemm(ref, p)
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+
+
+def test_gemm_prequant_entry():
+    """quant_a_packed + gemm_prequant equals the fused call."""
+    name = "m64_n7168_k2048"
+    ref = reference(name)
+    a = to_dev_bf16(ref["a_bits"])
+    M, K = ref["a_bits"].shape
+    N = ref["bq"].shape[0]
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    ap = mx.quant_a_packed(a)
+    c = mx.gemm_prequant(ap, M, b_packed, N, K)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bf16_out_to_f32(c), ref["c32"], "gemm_prequant")
+
+
+def test_library_quantized_b_matches_oracle_path():
+    """B quantized on the GPU by the library (the benchmark's route) gives the
+    same packed bytes as the oracle's B."""
+    _, b = inputs.make("m4_n2880_k512")
+    rq, rs = oracle.quantize(b)
+    bq, bs = mx.quant_a(to_dev_bf16(b))
+    p1 = mx.pack_b(bq, bs)
+    p2 = mx.pack_b(to_dev_u8(rq), to_dev_u8(rs))
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
