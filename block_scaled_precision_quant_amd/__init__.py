@@ -15,14 +15,16 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "library_path", "load", "packed_bytes",
-    "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "gemm",
+    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "REDUCE_KERNEL", "REDUCE_LAST_WG", "library_path", "load", "packed_bytes",
+    "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes", "gemm",
     "gemm_prequant", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 MODE_FUSED = 1
 MODE_PREQUANT = 2
+REDUCE_KERNEL = 0
+REDUCE_LAST_WG = 1
 
 _ERR_NAMES = {-1: "EINVAL", -2: "ENULL", -3: "EWORKSPACE", -4: "ESIZE", -5: "ENOTSUP", -6: "EHIP"}
 
@@ -37,7 +39,7 @@ class _CPlan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("m_blocks", ctypes.c_int),
                 ("n_tiles_per_wave", ctypes.c_int), ("waves_n", ctypes.c_int),
                 ("waves_k", ctypes.c_int), ("k_steps_per_wave", ctypes.c_int),
-                ("split_k", ctypes.c_int)]
+                ("split_k", ctypes.c_int), ("split_reduce", ctypes.c_int)]
 
 
 @dataclass(frozen=True)
@@ -50,10 +52,11 @@ class Plan:
     waves_k: int
     k_steps_per_wave: int
     split_k: int
+    split_reduce: int = 1  # REDUCE_LAST_WG
 
     def _c(self):
         return _CPlan(self.mode, self.m_blocks, self.n_tiles_per_wave, self.waves_n, self.waves_k,
-                      self.k_steps_per_wave, self.split_k)
+                      self.k_steps_per_wave, self.split_k, self.split_reduce)
 
 
 _LIB = None
@@ -70,7 +73,9 @@ _SIGNATURES = {
     "mxfp4_default_plan": (_i, [_i, _i, _i, ctypes.POINTER(_CPlan)]),
     "mxfp4_check_plan": (_i, [ctypes.POINTER(_CPlan), _i, _i, _i]),
     "mxfp4_plan_workspace_bytes": (_sz, [ctypes.POINTER(_CPlan), _i, _i, _i]),
+    "mxfp4_plan_workspace_zero_bytes": (_sz, [ctypes.POINTER(_CPlan), _i, _i, _i]),
     "mxfp4_gemm_workspace_bytes": (_sz, [_i, _i, _i]),
+    "mxfp4_gemm_prequant_workspace_bytes": (_sz, [ctypes.POINTER(_CPlan), _i, _i, _i]),
     "mxfp4_gemm": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "mxfp4_gemm_ex": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz,
                            ctypes.POINTER(_CPlan), _vp]),
@@ -177,7 +182,7 @@ def default_plan(M, N, K):
     p = _CPlan()
     _check(load().mxfp4_default_plan(M, N, K, ctypes.byref(p)))
     return Plan(p.mode, p.m_blocks, p.n_tiles_per_wave, p.waves_n, p.waves_k,
-                p.k_steps_per_wave, p.split_k)
+                p.k_steps_per_wave, p.split_k, p.split_reduce)
 
 
 def check_plan(plan, M, N, K):
@@ -193,13 +198,29 @@ def workspace_bytes(M, N, K, plan=None):
     return int(load().mxfp4_plan_workspace_bytes(ctypes.byref(cp), M, N, K))
 
 
-def _workspace(nbytes, device, workspace):
+def workspace_zero_bytes(M, N, K, plan=None):
+    """Leading workspace bytes that must be zero before first use."""
+    p = plan if plan is not None else default_plan(M, N, K)
+    cp = p._c()
+    return int(load().mxfp4_plan_workspace_zero_bytes(ctypes.byref(cp), M, N, K))
+
+
+def prequant_workspace_bytes(M, N, K, plan=None):
+    cp = plan._c() if plan is not None else None
+    return int(load().mxfp4_gemm_prequant_workspace_bytes(
+        ctypes.byref(cp) if cp is not None else None, M, N, K))
+
+
+def new_workspace(nbytes, device):
+    """A zero-filled workspace (its tile counters start at zero)."""
     import torch
-    if nbytes == 0:
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0 or workspace is not None:
         return workspace
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return workspace
+    return new_workspace(nbytes, device)
 
 
 def gemm(a, b_packed, N, out=None, workspace=None, plan=None, stream=None):
@@ -224,8 +245,7 @@ def gemm_prequant(a_packed, M, b_packed, N, K, out=None, workspace=None, plan=No
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_packed.device)
     p = plan if plan is not None else default_plan(M, N, K)
-    need = p.split_k * M * N * 4 if p.split_k > 1 else 0
-    workspace = _workspace(need, a_packed.device, workspace)
+    workspace = _workspace(prequant_workspace_bytes(M, N, K, p), a_packed.device, workspace)
     cp = p._c()
     _check(load().mxfp4_gemm_prequant(_ptr(a_packed), _nbytes(a_packed), _ptr(b_packed),
                                       _nbytes(b_packed), _ptr(out), out.stride(0), M, N, K,

@@ -44,11 +44,14 @@ mx::Plan to_internal(const mxfp4_plan& p) {
   q.wk = p.waves_k;
   q.ksw = p.k_steps_per_wave;
   q.split = p.split_k;
+  q.last_wg = p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_LAST_WG;
   return q;
 }
 
-mxfp4_plan make_plan(int mode, int mbw, int ntw, int wn, int wk, int ksw, int split) {
+mxfp4_plan make_plan(int mode, int mbw, int ntw, int wn, int wk, int ksw, int split,
+                     int reduce = MXFP4_REDUCE_KERNEL) {
   mxfp4_plan p;
+  p.split_reduce = reduce;
   p.mode = mode;
   p.m_blocks = mbw;
   p.n_tiles_per_wave = ntw;
@@ -74,6 +77,12 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
       p.k_steps_per_wave < 1 || p.split_k < 1)
     return fail(MXFP4_EINVAL, "plan fields must all be >= 1");
+  if (p.split_reduce != MXFP4_REDUCE_KERNEL && p.split_reduce != MXFP4_REDUCE_LAST_WG)
+    return fail(MXFP4_EINVAL, "plan.split_reduce must be MXFP4_REDUCE_KERNEL or MXFP4_REDUCE_LAST_WG (got %d)",
+                p.split_reduce);
+  if (p.split_k > mx::kMaxLastWgSplit && p.split_reduce == MXFP4_REDUCE_LAST_WG)
+    return fail(MXFP4_EINVAL, "split_reduce LAST_WG supports split_k <= %d (got %d)", mx::kMaxLastWgSplit,
+                p.split_k);
   const int mode = mode_matters ? p.mode : MXFP4_MODE_PREQUANT;
   if (!mx::gemm_kernel_available(mode, p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave))
     return fail(MXFP4_ENOTSUP,
@@ -96,12 +105,25 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   return MXFP4_OK;
 }
 
-size_t plan_workspace(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
-  size_t bytes = 0;
+// Workspace layout: [tile counters][MX-packed A][fp32 partials], each part
+// rounded up to 256 bytes.
+struct WsLayout {
+  size_t counters, a, partials;  // byte sizes
+  size_t a_off() const { return counters; }
+  size_t part_off() const { return counters + a; }
+  size_t total() const { return counters + a + partials; }
+};
+
+WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
+  WsLayout w = {0, 0, 0};
+  if (p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_LAST_WG) {
+    const mx::GemmGeom g = mx::gemm_geometry(to_internal(p), M, N, K);
+    w.counters = round_up((size_t)g.mgroups * g.ngroups * 4, 256);
+  }
   if (!prequant_entry && p.mode == MXFP4_MODE_PREQUANT)
-    bytes += round_up(mxfp4_packed_bytes(M, K), 256);
-  if (p.split_k > 1) bytes += (size_t)p.split_k * M * N * 4;
-  return bytes;
+    w.a = round_up(mxfp4_packed_bytes(M, K), 256);
+  if (p.split_k > 1) w.partials = round_up((size_t)p.split_k * M * N * 4, 256);
+  return w;
 }
 
 // Per-shape table for the tuned shapes, heuristic otherwise.
@@ -110,13 +132,15 @@ mxfp4_plan default_plan(int M, int N, int K) {
     int M, N, K;
     mxfp4_plan p;
   };
+  // Chosen by an L2-cold sweep over every valid plan on MI355X (median
+  // event time per call).
   static const Row table[] = {
-      {4, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 1, 1, 4, 1)},
-      {32, 4096, 512, make_plan(MXFP4_MODE_FUSED, 2, 1, 2, 1, 4, 1)},
-      {32, 2880, 512, make_plan(MXFP4_MODE_FUSED, 2, 1, 2, 1, 4, 1)},
-      {16, 2112, 7168, make_plan(MXFP4_MODE_PREQUANT, 1, 1, 1, 2, 7, 4)},
-      {64, 7168, 2048, make_plan(MXFP4_MODE_PREQUANT, 4, 1, 2, 1, 16, 1)},
-      {256, 3072, 1536, make_plan(MXFP4_MODE_PREQUANT, 4, 1, 4, 1, 12, 1)},
+      {4, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
+      {32, 4096, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
+      {32, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
+      {16, 2112, 7168, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 2, 4, 7, MXFP4_REDUCE_KERNEL)},
+      {64, 7168, 2048, make_plan(MXFP4_MODE_FUSED, 1, 1, 8, 1, 16, 1)},
+      {256, 3072, 1536, make_plan(MXFP4_MODE_FUSED, 1, 2, 8, 1, 12, 1)},
   };
   for (const Row& r : table)
     if (r.M == M && r.N == N && r.K == K) return r.p;
@@ -162,6 +186,14 @@ mxfp4_plan default_plan(int M, int N, int K) {
     }
   }
   return p;
+}
+
+int check_workspace(const void* workspace, size_t have, size_t need) {
+  if (need == 0) return MXFP4_OK;
+  if (!workspace) return fail(MXFP4_ENULL, "workspace is NULL but the plan needs %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MXFP4_EWORKSPACE, "workspace holds %zu bytes, plan needs %zu", have, need);
+  return MXFP4_OK;
 }
 
 int check_stream_ptrs(const void* p, const char* name) {
@@ -259,13 +291,27 @@ int mxfp4_check_plan(const mxfp4_plan* plan, int M, int N, int K) {
 size_t mxfp4_plan_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
   if (!plan || check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
   if (check_plan(*plan, M, N, K, true) != MXFP4_OK) return 0;
-  return plan_workspace(*plan, M, N, K, false);
+  return ws_layout(*plan, M, N, K, false).total();
+}
+
+size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan* plan, int M, int N, int K) {
+  if (!plan || check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
+  if (check_plan(*plan, M, N, K, false) != MXFP4_OK) return 0;
+  return ws_layout(*plan, M, N, K, false).counters;
+}
+
+size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
+  if (check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
+  mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
+  p.mode = MXFP4_MODE_PREQUANT;
+  if (check_plan(p, M, N, K, false) != MXFP4_OK) return 0;
+  return ws_layout(p, M, N, K, true).total();
 }
 
 size_t mxfp4_gemm_workspace_bytes(int M, int N, int K) {
   if (check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
   const mxfp4_plan p = default_plan(M, N, K);
-  return plan_workspace(p, M, N, K, false);
+  return ws_layout(p, M, N, K, false).total();
 }
 
 int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
@@ -285,25 +331,20 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
     return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
   const mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
   if ((rc = check_plan(p, M, N, K, true))) return rc;
-  const size_t wneed = plan_workspace(p, M, N, K, false);
-  if (wneed > 0) {
-    if (!workspace) return fail(MXFP4_ENULL, "workspace is NULL but the plan needs %zu bytes", wneed);
-    if (!aligned(workspace, 256)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
-    if (workspace_bytes < wneed)
-      return fail(MXFP4_EWORKSPACE, "workspace holds %zu bytes, plan needs %zu", workspace_bytes, wneed);
-  }
+  const WsLayout wl = ws_layout(p, M, N, K, false);
+  if ((rc = check_workspace(workspace, workspace_bytes, wl.total()))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const void* a_src = a;
   if (p.mode == MXFP4_MODE_PREQUANT) {
-    mx::launch_quant_packed(a, M, K, lda, ws, st);
+    mx::launch_quant_packed(a, M, K, lda, ws + wl.a_off(), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "quant_a_packed launch");
-    a_src = ws;
-    ws += round_up(mxfp4_packed_bytes(M, K), 256);
+    a_src = ws + wl.a_off();
   }
   hipError_t e = mx::launch_gemm(to_internal(p), a_src, lda, static_cast<const uint8_t*>(b_packed), c,
-                                 ldc, M, N, K, reinterpret_cast<float*>(ws), st);
+                                 ldc, M, N, K, reinterpret_cast<float*>(ws + wl.part_off()),
+                                 reinterpret_cast<unsigned*>(ws), st);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }
@@ -335,16 +376,12 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
   mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
   p.mode = MXFP4_MODE_PREQUANT;
   if ((rc = check_plan(p, M, N, K, false))) return rc;
-  const size_t wneed = plan_workspace(p, M, N, K, true);
-  if (wneed > 0) {
-    if (!workspace) return fail(MXFP4_ENULL, "workspace is NULL but the plan needs %zu bytes", wneed);
-    if (!aligned(workspace, 256)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
-    if (workspace_bytes < wneed)
-      return fail(MXFP4_EWORKSPACE, "workspace holds %zu bytes, plan needs %zu", workspace_bytes, wneed);
-  }
+  const WsLayout wl = ws_layout(p, M, N, K, true);
+  if ((rc = check_workspace(workspace, workspace_bytes, wl.total()))) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t e = mx::launch_gemm(to_internal(p), a_packed, 0, static_cast<const uint8_t*>(b_packed), c,
-                                 ldc, M, N, K, static_cast<float*>(workspace),
-                                 static_cast<hipStream_t>(stream));
+                                 ldc, M, N, K, reinterpret_cast<float*>(ws + wl.part_off()),
+                                 reinterpret_cast<unsigned*>(ws), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }

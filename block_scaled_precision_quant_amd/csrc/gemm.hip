@@ -26,10 +26,14 @@ struct GemmArgs {
   const uint8_t* bp;  // MX-packed B
   uint16_t* c;        // bf16 C [M][ldc]
   float* ws;          // fp32 partials [split][M][N]
+  unsigned* counters; // per output tile arrival counters (last-workgroup reduce)
   int M, N, K, lda, ldc;
   int MT, NT, KS, KG;
   int wn, wk, split, mgroups, ngroups, kswg;
+  int last_wg_reduce;  // split > 1: 1 = last workgroup sums, 0 = reduce kernel
   unsigned lds_asc_off, lds_red_off, lds_raw_off;
+  unsigned cpr_inv;  // floor(2^32 / (16*kswg)) + 1: x / (16*kswg) == umulhi(x, cpr_inv)
+                     // for every x < 2^32 / (16*kswg)
 };
 
 // LDS-direct loads: each active lane moves 16 (or 4) bytes from its own
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
     for (int ci = wave; ci * 64 < n_chunks; ci += nwaves) {
       const int flat = ci * 64 + lane;
       if (flat < n_chunks) {
-        const int r = flat / chunks_per_row;
+        const int r = (int)__umulhi((unsigned)flat, g.cpr_inv);
         const int c = flat - r * chunks_per_row;
         lds_load16(g.a + (size_t)(m0 + r) * g.lda + (size_t)jw0 * kStep + (size_t)c * 8,
                    lds_raw + (size_t)ci * 1024);
@@ -145,9 +149,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
     // the 4 items of an aligned quad of lanes form one 32-element group.
     const int chunks_per_row = kswg * 16;
     const int n_items = rows_valid * chunks_per_row;
-    int r = tid / chunks_per_row;
-    int c = tid - r * chunks_per_row;
     for (int it = tid; it < n_items; it += nthreads) {
+      const int r = (int)__umulhi((unsigned)it, g.cpr_inv);
+      const int c = it - r * chunks_per_row;
       const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + (size_t)it * 16);
       const int jl = c >> 4;
       const int kg = (c >> 2) & 3;
@@ -155,18 +159,13 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
       const int jj = jw0 + jl;
       const uint32_t amax = quad_max(amax8_bits(v));
       const uint32_t byte = scale_byte_from_amax(amax);
-      const uint32_t codes = encode8(v, inv_scale_from_byte(byte));
+      const uint32_t codes = encode8(v, byte);
       const int b = r >> 4;
       const int ln = (r & 15) + 16 * kg;
       *reinterpret_cast<uint32_t*>(lds_a + ((size_t)(b * kswg + jl) * 64 + ln) * 16 + 4 * p) =
           codes;
       if (p == 0)
         lds_sc[((size_t)(b * ngw + (jj >> 2) - gw0) * 64 + ln) * 4 + (jj & 3)] = (uint8_t)byte;
-      c += nthreads;
-      while (c >= chunks_per_row) {
-        c -= chunks_per_row;
-        ++r;
-      }
     }
     __syncthreads();
   }
@@ -241,10 +240,13 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   }
 
   // ---- 4. sum the wk wavefronts of one column group in LDS, in order.
+  //         Every wavefront stays to the end so that each barrier below is
+  //         reached by the whole workgroup; only wave_k == 0 stores.
+  const bool owner = wave_k == 0;
   if (g.wk > 1) {
     float* red = reinterpret_cast<float*>(smem + g.lds_red_off);
     constexpr int per_wave = MBW * NTW * 256;
-    if (wave_k > 0) {
+    if (!owner) {
       float* dst = red + (size_t)((wave_k - 1) * g.wn + wave_n) * per_wave;
 #pragma unroll
       for (int b = 0; b < MBW; ++b)
@@ -253,36 +255,100 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
           *reinterpret_cast<f32x4*>(dst + ((b * NTW + i) * 64 + lane) * 4) = acc[b][i];
     }
     __syncthreads();
-    if (wave_k > 0) return;
-    for (int kk = 1; kk < g.wk; ++kk) {
-      const float* src = red + (size_t)((kk - 1) * g.wn + wave_n) * per_wave;
+    if (owner) {
+      for (int kk = 1; kk < g.wk; ++kk) {
+        const float* src = red + (size_t)((kk - 1) * g.wn + wave_n) * per_wave;
 #pragma unroll
-      for (int b = 0; b < MBW; ++b)
+        for (int b = 0; b < MBW; ++b)
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
-          acc[b][i] += *reinterpret_cast<const f32x4*>(src + ((b * NTW + i) * 64 + lane) * 4);
+          for (int i = 0; i < NTW; ++i)
+            acc[b][i] += *reinterpret_cast<const f32x4*>(src + ((b * NTW + i) * 64 + lane) * 4);
+      }
     }
   }
 
   // ---- 5. store: bf16 (nearest even) or an fp32 partial.
+  if (owner) {
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    const int nt = nt_base + i;
-    if (nt >= g.NT) continue;
-    const int col = nt * 16 + (lane & 15);
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = nt_base + i;
+      if (nt >= g.NT) continue;
+      const int col = nt * 16 + (lane & 15);
 #pragma unroll
-    for (int b = 0; b < MBW; ++b) {
+      for (int b = 0; b < MBW; ++b) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
-        if (row >= g.M) continue;
-        if (g.split == 1)
-          g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[b][i][e]);
-        else
-          g.ws[((size_t)s * g.M + row) * g.N + col] = acc[b][i][e];
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
+          if (row >= g.M) continue;
+          float* part = g.ws + ((size_t)s * g.M + row) * g.N + col;
+          if (g.split == 1)
+            g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[b][i][e]);
+          else if (g.last_wg_reduce)
+            __hip_atomic_store(part, acc[b][i][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            *part = acc[b][i][e];
+        }
       }
     }
   }
+  if (g.split == 1 || !g.last_wg_reduce) return;
+
+  // ---- 6. split-K finished by the last workgroup of this output tile.
+  //         The partials above are agent-scope atomic stores, which are
+  //         coherent across the XCDs' L2 caches without an L2 write-back;
+  //         once they have completed (waitcnt) the tile counter is bumped,
+  //         and the workgroup that takes it to split-1 reads the partials
+  //         with agent-scope atomic loads, sums them in order
+  //         s = 0..split-1 (the order of splitk_reduce_kernel, so both
+  //         reductions give identical bits) and returns the counter to zero
+  //         for the next call on this workspace.  The flag lives in the first
+  //         LDS word: every LDS read above is behind the first barrier here.
+  volatile int* is_last = reinterpret_cast<volatile int*>(smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int tile = mg * g.ngroups + ng;
+  if (tid == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *is_last = (old == (unsigned)(g.split - 1));
+  }
+  __syncthreads();
+  if (!*is_last) return;
+  if (owner) {
+    const size_t plane = (size_t)g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = nt_base + i;
+      if (nt >= g.NT) continue;
+      const int col = nt * 16 + (lane & 15);
+#pragma unroll
+      for (int b = 0; b < MBW; ++b) {
+        // all split partials of this lane's 4 outputs are requested before
+        // the first is summed (rows >= M read row 0 and are not stored)
+        float v[4][kMaxLastWgSplit];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = min(m0 + b * 16 + 4 * (lane >> 4) + e, g.M - 1);
+          float* src = g.ws + (size_t)row * g.N + col;
+#pragma unroll
+          for (int k = 0; k < kMaxLastWgSplit; ++k)
+            if (k < g.split)
+              v[e][k] = __hip_atomic_load(src + (size_t)k * plane, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
+          float sum = v[e][0];
+#pragma unroll
+          for (int k = 1; k < kMaxLastWgSplit; ++k)
+            if (k < g.split) sum += v[e][k];
+          if (row < g.M) g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(sum);
+        }
+      }
+    }
+  }
+  if (tid == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Sum split fp32 partials [S][M][N] in order s = 0..S-1 and round to bf16.
@@ -397,7 +463,7 @@ GemmGeom gemm_geometry(const Plan& p, int M, int N, int K) {
 
 hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_packed,
                        uint16_t* c, int ldc, int M, int N, int K, float* ws,
-                       hipStream_t stream) {
+                       unsigned* counters, hipStream_t stream) {
   const int ki = find_kernel(p.mode, p.mbw, p.ntw, p.ksw);
   if (ki < 0) return hipErrorInvalidDeviceFunction;
   const GemmGeom geo = gemm_geometry(p, M, N, K);
@@ -413,6 +479,8 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   args.bp = b_packed;
   args.c = c;
   args.ws = ws;
+  args.counters = counters;
+  args.last_wg_reduce = p.last_wg ? 1 : 0;
   args.M = M;
   args.N = N;
   args.K = K;
@@ -431,11 +499,12 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   args.lds_asc_off = (unsigned)geo.lds_a;
   args.lds_red_off = (unsigned)(geo.lds_a + geo.lds_asc);
   args.lds_raw_off = args.lds_red_off;
+  args.cpr_inv = (unsigned)((1ull << 32) / (16ull * geo.kswg) + 1);
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(fn, dim3(geo.grid), dim3(geo.threads), kargs,
                                  (unsigned)geo.lds_total, stream);
   if (e != hipSuccess) return e;
-  if (p.split > 1) {
+  if (p.split > 1 && !p.last_wg) {
     const long long n = (long long)M * (N / 4);
     const unsigned grid = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, M, N, ldc,

@@ -18,9 +18,11 @@ struct Plan {
   int wk;        // wavefronts along K
   int ksw;       // 128-K steps per wavefront
   int split;     // workgroups along K
+  int last_wg;   // split > 1: the last workgroup of a tile sums the partials
 };
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxLastWgSplit = 16;  // split_k bound for the last-workgroup reduce
 constexpr int kMaxThreads = 512;
 
 // Launch geometry derived from a plan and a shape.
@@ -43,11 +45,13 @@ GemmGeom gemm_geometry(const Plan& p, int M, int N, int K);
 // True when a kernel for (mode, mbw, ntw, ksw) is compiled in.
 bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw);
 
-// Enqueue the GEMM kernel (and the split-K reduce when p.split > 1).
-//   a: bf16 A (fused) or MX-packed A (prequant); ws: fp32 partials.
+// Enqueue the GEMM kernel (and the split-K reduce kernel when p.split > 1
+// and !p.last_wg).
+//   a: bf16 A (fused) or MX-packed A (prequant); ws: fp32 partials;
+//   counters: mgroups*ngroups zeroed tile counters (p.last_wg only).
 hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_packed,
                        uint16_t* c, int ldc, int M, int N, int K, float* ws,
-                       hipStream_t stream);
+                       unsigned* counters, hipStream_t stream);
 
 void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
                          uint8_t* out_scale, int ld_scale, hipStream_t stream);

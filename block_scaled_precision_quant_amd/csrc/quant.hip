@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void quant_linear_kernel(const uint16_t* __res
   const uint4 v = *reinterpret_cast<const uint4*>(a + (size_t)row * lda + (size_t)kk * 8);
   const uint32_t amax = quad_max(amax8_bits(v));
   const uint32_t byte = scale_byte_from_amax(amax);
-  const uint32_t codes = encode8(v, inv_scale_from_byte(byte));
+  const uint32_t codes = encode8(v, byte);
   *reinterpret_cast<uint32_t*>(out_fp4 + (size_t)row * ld_fp4 + (size_t)kk * 4) = codes;
   if ((kk & 3) == 0) out_scale[(size_t)row * ld_scale + (kk >> 2)] = (uint8_t)byte;
 }
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void quant_packed_kernel(const uint16_t* __res
     const uint4 v = *reinterpret_cast<const uint4*>(a + (size_t)row * lda + (size_t)kk * 8);
     const uint32_t amax = quad_max(amax8_bits(v));
     byte = scale_byte_from_amax(amax);
-    codes = encode8(v, inv_scale_from_byte(byte));
+    codes = encode8(v, byte);
   }
   *reinterpret_cast<uint32_t*>(out + d.data_off(t, j, lane) + 4 * p) = codes;
   if (p == 0) {

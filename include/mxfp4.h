@@ -106,8 +106,12 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * k_steps_per_wave 128-element K-steps.  The K steps must be covered
  * exactly: split_k * waves_k * k_steps_per_wave == K/128.  waves_k > 1 sums
  * the wavefronts' partial tiles in LDS (fixed order); split_k > 1 writes fp32
- * partials [split_k][M][N] to the workspace and a reduce pass sums them in
- * order s = 0..split_k-1 and rounds to bf16 (nearest even).
+ * partials [split_k][M][N] to the workspace and sums them in order
+ * s = 0..split_k-1, rounding to bf16 (nearest even) -- either in a separate
+ * reduce kernel (split_reduce = MXFP4_REDUCE_KERNEL) or, in the same launch,
+ * in the last workgroup to finish each output tile, found with a per-tile
+ * arrival counter in the workspace (MXFP4_REDUCE_LAST_WG).  Both give the
+ * same bits.
  *
  * mode FUSED quantizes the workgroup's A rows inside the GEMM kernel; mode
  * PREQUANT first runs the quantizer once into the workspace (MX-packed) and
@@ -115,6 +119,9 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1
 #define MXFP4_MODE_PREQUANT 2
+
+#define MXFP4_REDUCE_KERNEL 0
+#define MXFP4_REDUCE_LAST_WG 1
 
 typedef struct mxfp4_plan {
     int mode;             /* MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT */
@@ -124,6 +131,8 @@ typedef struct mxfp4_plan {
     int waves_k;          /* wavefronts along K per workgroup (in-LDS reduce) */
     int k_steps_per_wave; /* 128-K steps per wavefront: 1,2,3,4,6,7,8,12,14,16 */
     int split_k;          /* workgroups along K (fp32 workspace + reduce) */
+    int split_reduce;     /* split_k > 1: MXFP4_REDUCE_KERNEL or MXFP4_REDUCE_LAST_WG
+                             (LAST_WG needs split_k <= 16) */
 } mxfp4_plan;
 
 /* The plan mxfp4_gemm uses for a shape (a per-shape table for the tuned
@@ -135,12 +144,22 @@ int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
  * ENULL), with the reason in mxfp4_last_error(). */
 int mxfp4_check_plan(const mxfp4_plan *plan, int M, int N, int K);
 
-/* Workspace bytes a plan needs for a shape: the MX-packed A in PREQUANT
- * mode (rounded up to 256 bytes) plus split_k*M*N*4 bytes of fp32 partials
- * when split_k > 1.  0 when none is needed or the plan is invalid. */
+/* Workspace bytes a plan needs for a shape, laid out as
+ *   [tile counters][MX-packed A][fp32 partials]
+ * with each part rounded up to 256 bytes: tile counters (4 bytes per
+ * workgroup tile) when split_k > 1 and split_reduce is LAST_WG; the MX-packed
+ * A in PREQUANT mode; split_k*M*N*4 bytes of partials when split_k > 1.
+ * 0 when none is needed or the plan is invalid. */
 size_t mxfp4_plan_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
 
-/* Workspace bytes of the default plan. */
+/* Leading workspace bytes (the tile counters) that must be zero before the
+ * first call that uses the workspace with this plan; every completed call
+ * leaves them zero again, so one zero-fill per workspace suffices.  Calls
+ * that share one workspace must not overlap in time.  The rest of the
+ * workspace is scratch.  0 when the plan keeps no counters. */
+size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan *plan, int M, int N, int K);
+
+/* Workspace bytes of the default plan (same layout and zero-fill rule). */
 size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
 
 /* C = A . B^T with the default plan.
@@ -149,7 +168,9 @@ size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
  *             mxfp4_packed_bytes(N, K);
  *   c         [M][ldc] bf16 output, ldc >= N; only the M x N block is written;
  *   workspace device scratch of at least mxfp4_gemm_workspace_bytes(M,N,K)
- *             bytes, 256-byte aligned (may be NULL when that is 0).
+ *             bytes, 256-byte aligned (may be NULL when that is 0), whose
+ *             leading zero-bytes (see mxfp4_plan_workspace_zero_bytes) were
+ *             zero-filled once before first use.
  * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
  * Inputs are finite.  Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
 int mxfp4_gemm(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
@@ -164,8 +185,13 @@ int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_pac
 /* GEMM on an A that is already MX-packed (from mxfp4_quant_a_packed), for
  * callers that quantize one activation once and use it against several
  * weights.  The plan's mode is ignored (the kernel reads fp4 A); NULL plan =
- * the default plan's tiling.  Workspace: split_k*M*N*4 bytes when split_k > 1.
+ * the default plan's tiling.  Workspace: as for mxfp4_gemm_ex with the plan in
+ * PREQUANT mode, minus the MX-packed A part (tile counters, then partials).
  * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
+/* Workspace bytes of mxfp4_gemm_prequant for a plan (NULL = default plan);
+ * its zero-fill prefix is mxfp4_plan_workspace_zero_bytes of the same plan. */
+size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
+
 int mxfp4_gemm_prequant(const void *a_packed, size_t a_packed_bytes, const void *b_packed,
                         size_t b_packed_bytes, uint16_t *c, int ldc, int M, int N, int K,
                         void *workspace, size_t workspace_bytes, const mxfp4_plan *plan,

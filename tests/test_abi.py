@@ -97,9 +97,20 @@ def test_gemm_rejects_bad_plans_and_workspace(lib):
     # fused stage of 64 rows x 2048 K in LDS does not fit
     assert call(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 1, 16, 1)) == EINVAL
     assert "LDS" in mx.load().mxfp4_last_error().decode()
-    split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4)
-    assert mx.workspace_bytes(M, N, K, split) == 4 * M * N * 4
-    assert call(split, FAKE, 4 * M * N * 4 - 4) == EWORKSPACE
+    # split-K: [tile counters][partials]; counters only for the last-WG reduce
+    split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
+    tiles = 4 * 16  # (64/16)/1 row groups x (256/16)/1 column groups
+    assert mx.workspace_zero_bytes(M, N, K, split) == 256 == -(-tiles * 4 // 256) * 256
+    assert mx.workspace_bytes(M, N, K, split) == 256 + 4 * M * N * 4
+    assert call(split, FAKE, 256 + 4 * M * N * 4 - 4) == EWORKSPACE
+    split_k = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_KERNEL)
+    assert mx.workspace_zero_bytes(M, N, K, split_k) == 0
+    assert mx.workspace_bytes(M, N, K, split_k) == 4 * M * N * 4
+    assert call(mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, 7)) == EINVAL  # split_reduce
+    pq = mx.Plan(mx.MODE_PREQUANT, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
+    assert mx.workspace_bytes(M, N, K, pq) == 256 + (mx.packed_bytes(M, K) + 255) // 256 * 256 \
+        + 4 * M * N * 4
+    assert mx.prequant_workspace_bytes(M, N, K, pq) == 256 + 4 * M * N * 4
 
 
 def test_quant_and_pack_reject_bad_arguments(lib):

@@ -43,13 +43,20 @@ def run_gemm(ref, plan=None, poison=True):
     N = ref["bq"].shape[0]
     b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
     c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=a.device)
-    ws = None
-    nws = mx.workspace_bytes(M, N, K, plan)
-    if nws:
-        ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=a.device)  # NaN poison
+    ws = workspace(M, N, K, plan, a.device)
     mx.gemm(a, b_packed, N, out=c, workspace=ws, plan=plan)
     torch.cuda.synchronize()
     return bf16_out_to_f32(c)
+
+
+def workspace(M, N, K, plan, device):
+    """Workspace with zeroed tile counters and NaN-poisoned scratch."""
+    nws = mx.workspace_bytes(M, N, K, plan)
+    if not nws:
+        return None
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=device)
+    ws[:mx.workspace_zero_bytes(M, N, K, plan)] = 0
+    return ws
 
 
 @pytest.mark.parametrize("name", inputs.ORDER)
@@ -138,6 +145,36 @@ def test_lane_map_one_hot():
     for m in range(M):
         np.testing.assert_array_equal(got[m], inputs.bf16_bits_to_f32(
             inputs.f32_to_bf16_bits(ref["bd"][:, ks[m]].astype(np.float32))))
+
+
+@pytest.mark.parametrize("name,plan", [
+    ("m16_n2112_k7168", mx.Plan(F, 1, 1, 4, 2, 4, 7)),
+    ("m16_n2112_k7168", mx.Plan(P, 1, 1, 1, 2, 7, 4)),
+    ("m64_n7168_k2048", mx.Plan(F, 4, 1, 2, 1, 4, 4)),
+    ("m4_n2880_k512", mx.Plan(F, 1, 2, 1, 1, 1, 4)),
+])
+def test_split_reduce_modes_agree(name, plan):
+    """Last-workgroup reduce and the reduce kernel give the same bits, and a
+    reused workspace (counters back at zero) gives them again."""
+    w = inputs.WORKLOADS[name]
+    print("case", name, plan, flush=True)
+    ref = reference(name)
+    a = to_dev_bf16(ref["a_bits"])
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    outs = []
+    for reduce in (mx.REDUCE_KERNEL, mx.REDUCE_LAST_WG):
+        p = mx.Plan(*(list(plan.__dict__.values())[:7] + [reduce]))
+        ws = workspace(w.M, w.N, w.K, p, a.device)
+        for _ in range(3):
+            c = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device=a.device)
+            mx.gemm(a, b_packed, w.N, out=c, workspace=ws, plan=p)
+            torch.cuda.synchronize()
+            outs.append(bf16_out_to_f32(c))
+        nz = mx.workspace_zero_bytes(w.M, w.N, w.K, p)
+        assert int(ws[:nz].count_nonzero()) == 0  # counters returned to zero
+    assert_close_to_oracle(outs[0], ref["c32"], "%s %s" % (name, plan))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
 def test_bitwise_repeatable():
