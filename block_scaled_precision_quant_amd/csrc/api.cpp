@@ -7,7 +7,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "../../include/mxfp4.h"
+#include "mxfp4.h"
 #include "mx_internal.hpp"
 
 namespace {
@@ -100,7 +100,7 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   const mx::GemmGeom g = mx::gemm_geometry(q, M, N, K);
   if (g.lds_total > (size_t)mx::kMaxLds)
     return fail(MXFP4_EINVAL, "plan needs %zu bytes of LDS (max %d)", g.lds_total, mx::kMaxLds);
-  if ((long long)g.mgroups * g.ngroups * p.split_k > 0x7FFFFFFFLL)
+  if (8LL * ((long long)g.ngroups * p.split_k + 7) / 8 * g.mgroups > 0x7FFFFFFFLL)
     return fail(MXFP4_EINVAL, "grid too large");
   return MXFP4_OK;
 }
@@ -138,7 +138,7 @@ mxfp4_plan default_plan(int M, int N, int K) {
       {4, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
       {32, 4096, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
       {32, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
-      {16, 2112, 7168, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 2, 4, 7, MXFP4_REDUCE_KERNEL)},
+      {16, 2112, 7168, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 2, 7, 4, MXFP4_REDUCE_KERNEL)},
       {64, 7168, 2048, make_plan(MXFP4_MODE_FUSED, 1, 1, 8, 1, 16, 1)},
       {256, 3072, 1536, make_plan(MXFP4_MODE_FUSED, 1, 2, 8, 1, 12, 1)},
   };

@@ -31,9 +31,9 @@ struct GemmArgs {
   int MT, NT, KS, KG;
   int wn, wk, split, mgroups, ngroups, kswg;
   int last_wg_reduce;  // split > 1: 1 = last workgroup sums, 0 = reduce kernel
-  unsigned lds_asc_off, lds_red_off, lds_raw_off;
-  unsigned cpr_inv;  // floor(2^32 / (16*kswg)) + 1: x / (16*kswg) == umulhi(x, cpr_inv)
-                     // for every x < 2^32 / (16*kswg)
+  unsigned lds_asc_off, lds_red_off;
+  unsigned long long kswg_inv;  // floor(2^32 / kswg) + 1: x / kswg == (x * kswg_inv) >> 32
+                                // for every x < 2^32 / kswg (33-bit for kswg = 1)
 };
 
 // LDS-direct loads: each active lane moves 16 (or 4) bytes from its own
@@ -66,11 +66,19 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   const int wave_k = wave / g.wn;
   const int nthreads = blockDim.x;
 
-  int bid = blockIdx.x;
-  const int ng = bid % g.ngroups;
-  bid /= g.ngroups;
-  const int mg = bid % g.mgroups;
-  const int s = bid / g.mgroups;
+  // XCD-aware order: consecutive workgroup ids go to the 8 XCDs in turn, so
+  // workgroup i runs on XCD i % 8.  The mgroups row groups of one column
+  // task (same B tiles, same K range) get ids that are equal mod 8 and land
+  // on one XCD, where the first read of each B tile fills the L2 for the
+  // rest.  Ids past the last task (padding of the final round) exit at once.
+  const int tasks = g.ngroups * g.split;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int task = xcd + 8 * (slot / g.mgroups);
+  if (task >= tasks) return;
+  const int mg = slot % g.mgroups;
+  const int ng = task % g.ngroups;
+  const int s = task / g.ngroups;
 
   const int m0 = mg * MBW * 16;
   const int kswg = g.kswg;
@@ -80,7 +88,83 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   const int ngw = ((jw0 + kswg - 1) >> 2) - gw0 + 1;
   const int nt_base = (ng * g.wn + wave_n) * NTW;
 
-  // ---- 1. issue every B load of this wavefront (clamped tile index keeps a
+  // ---- 1. A for steps [jw0, jw0 + kswg).  Fused mode: the first kAPT raw
+  //         items of every thread are loaded into registers before any B
+  //         load is issued (addresses of unused items are clamped to a valid
+  //         one, so the number of load instructions is fixed and the
+  //         compiler's wait for them leaves the B loads in flight while A is
+  //         quantized).  Prequant mode: the packed A blocks are copied to LDS
+  //         by LDS-direct loads (global -> LDS without registers).
+  //
+  //         A fused item is 8 consecutive bf16 (16 bytes); the 4 items of an
+  //         aligned quad of lanes form one 32-element group, and a
+  //         wavefront's 64 items are 16 rows x 4 quarters of one (step,
+  //         K-group) -- 16 rows x 64 contiguous bytes in global memory and
+  //         64 consecutive LDS words for its codes (no bank conflicts).
+  const int nwaves = nthreads >> 6;
+  uint8_t* lds_a = smem;
+  uint8_t* lds_sc = smem + g.lds_asc_off;
+  const int rows_valid = min(MBW * 16, g.M - m0);
+  const int n_items = MODE == 1 ? ((rows_valid + 15) >> 4) * kswg * 256 : 0;
+  struct Item {
+    int r, jl, kg, p;
+    bool valid;
+  };
+  auto item = [&](int it) {
+    Item x;
+    x.p = it & 3;
+    const int r16 = (it >> 2) & 15;
+    x.kg = (it >> 6) & 3;
+    const int rest = it >> 8;
+    const int rg = (int)(((unsigned long long)rest * g.kswg_inv) >> 32);
+    x.jl = rest - rg * kswg;
+    x.r = rg * 16 + r16;
+    x.valid = it < n_items && x.r < rows_valid;  // uniform over a quad (same row)
+    return x;
+  };
+  auto item_ptr = [&](const Item& x) {
+    const int r = x.valid ? x.r : 0;
+    const size_t col = x.valid ? ((size_t)(jw0 + x.jl) * kStep + x.kg * 32 + x.p * 8)
+                               : (size_t)jw0 * kStep;
+    return reinterpret_cast<const uint4*>(g.a + (size_t)(m0 + r) * g.lda + col);
+  };
+  auto quantize_item = [&](const Item& x, uint4 v) {
+    const int jj = jw0 + x.jl;
+    const uint32_t amax = quad_max(amax8_bits(v));
+    const uint32_t byte = scale_byte_from_amax(amax);
+    const uint32_t codes = encode8(v, byte);
+    const int rg = x.r >> 4;
+    const int ln = (x.r & 15) + 16 * x.kg;
+    *reinterpret_cast<uint32_t*>(lds_a + ((size_t)(rg * kswg + x.jl) * 64 + ln) * 16 + 4 * x.p) =
+        codes;
+    if (x.p == 0)
+      lds_sc[((size_t)(rg * ngw + (jj >> 2) - gw0) * 64 + ln) * 4 + (jj & 3)] = (uint8_t)byte;
+  };
+  uint4 araw[kAPT];
+  if constexpr (MODE == 1) {
+#pragma unroll
+    for (int u = 0; u < kAPT; ++u) araw[u] = *item_ptr(item(tid + u * nthreads));
+  } else {
+    const PackedDims da = {g.MT, g.KS, g.KG};
+    const int mbv = min(MBW, g.MT - mg * MBW);
+    const int n_blocks = mbv * kswg;
+    for (int bi = wave; bi < n_blocks; bi += nwaves) {
+      const int b = bi / kswg;
+      const int jl = bi - b * kswg;
+      lds_load16(g.ap + da.data_off(mg * MBW + b, jw0 + jl, lane),
+                 lds_a + (size_t)(b * kswg + jl) * 1024);
+    }
+    const int n_sd = mbv * ngw;
+    for (int bi = wave; bi < n_sd; bi += nwaves) {
+      const int b = bi / ngw;
+      const int gl = bi - b * ngw;
+      lds_load4(g.ap + da.scale_off(mg * MBW + b, gw0 + gl, lane),
+                lds_sc + (size_t)(b * ngw + gl) * 256);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. issue every B load of this wavefront (clamped tile index keeps a
   //         ragged last group in bounds; its results are never stored).
   uint4 bq[NTW][KSW];
   uint32_t bs[NTW][NSD];
@@ -100,75 +184,26 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // ---- 2. stage the workgroup's A rows for steps [jw0, jw0 + kswg) in LDS.
-  //         All of it moves by LDS-direct loads (global -> LDS without
-  //         registers, 1 KiB or 256 B per wavefront instruction), issued
-  //         right behind the B loads so every global load of the workgroup is
-  //         in flight at once; one wait then covers both.
-  const int nwaves = nthreads >> 6;
-  uint8_t* lds_a = smem;
-  uint8_t* lds_sc = smem + g.lds_asc_off;
-  uint8_t* lds_raw = smem + g.lds_raw_off;
-  const int rows_valid = min(MBW * 16, g.M - m0);
   if constexpr (MODE == 1) {
-    // raw bf16 rows, row-major, kswg*256 bytes per row
-    const int chunks_per_row = kswg * 16;  // 16-byte chunks
-    const int n_chunks = rows_valid * chunks_per_row;
-    for (int ci = wave; ci * 64 < n_chunks; ci += nwaves) {
-      const int flat = ci * 64 + lane;
-      if (flat < n_chunks) {
-        const int r = (int)__umulhi((unsigned)flat, g.cpr_inv);
-        const int c = flat - r * chunks_per_row;
-        lds_load16(g.a + (size_t)(m0 + r) * g.lda + (size_t)jw0 * kStep + (size_t)c * 8,
-                   lds_raw + (size_t)ci * 1024);
+#pragma unroll
+    for (int u = 0; u < kAPT; ++u) {
+      const Item x = item(tid + u * nthreads);
+      if (x.valid) quantize_item(x, araw[u]);
+    }
+    // further rounds (plans whose A stage exceeds kAPT items per thread)
+    for (int base = kAPT * nthreads; base < n_items; base += kAPT * nthreads) {
+#pragma unroll
+      for (int u = 0; u < kAPT; ++u) araw[u] = *item_ptr(item(base + tid + u * nthreads));
+#pragma unroll
+      for (int u = 0; u < kAPT; ++u) {
+        const Item x = item(base + tid + u * nthreads);
+        if (x.valid) quantize_item(x, araw[u]);
       }
     }
   } else {
-    const PackedDims da = {g.MT, g.KS, g.KG};
-    const int mbv = min(MBW, g.MT - mg * MBW);
-    const int n_blocks = mbv * kswg;
-    for (int bi = wave; bi < n_blocks; bi += nwaves) {
-      const int b = bi / kswg;
-      const int jl = bi - b * kswg;
-      lds_load16(g.ap + da.data_off(mg * MBW + b, jw0 + jl, lane),
-                 lds_a + (size_t)(b * kswg + jl) * 1024);
-    }
-    const int n_sd = mbv * ngw;
-    for (int bi = wave; bi < n_sd; bi += nwaves) {
-      const int b = bi / ngw;
-      const int gl = bi - b * ngw;
-      lds_load4(g.ap + da.scale_off(mg * MBW + b, gw0 + gl, lane),
-                lds_sc + (size_t)(b * ngw + gl) * 256);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS-direct copies
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  if constexpr (MODE == 1) {
-    // Quantize the raw rows: one item = 8 consecutive bf16 (16 bytes), and
-    // the 4 items of an aligned quad of lanes form one 32-element group.
-    const int chunks_per_row = kswg * 16;
-    const int n_items = rows_valid * chunks_per_row;
-    for (int it = tid; it < n_items; it += nthreads) {
-      const int r = (int)__umulhi((unsigned)it, g.cpr_inv);
-      const int c = it - r * chunks_per_row;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + (size_t)it * 16);
-      const int jl = c >> 4;
-      const int kg = (c >> 2) & 3;
-      const int p = c & 3;
-      const int jj = jw0 + jl;
-      const uint32_t amax = quad_max(amax8_bits(v));
-      const uint32_t byte = scale_byte_from_amax(amax);
-      const uint32_t codes = encode8(v, byte);
-      const int b = r >> 4;
-      const int ln = (r & 15) + 16 * kg;
-      *reinterpret_cast<uint32_t*>(lds_a + ((size_t)(b * kswg + jl) * 64 + ln) * 16 + 4 * p) =
-          codes;
-      if (p == 0)
-        lds_sc[((size_t)(b * ngw + (jj >> 2) - gw0) * 64 + ln) * 4 + (jj & 3)] = (uint8_t)byte;
-    }
-    __syncthreads();
-  }
 
   // ---- 3. block-scaled FP4 products.  Rows >= M get scale byte 0 and are
   //         never stored.
@@ -452,11 +487,9 @@ GemmGeom gemm_geometry(const Plan& p, int M, int N, int K) {
   g.lds_a = (size_t)p.mbw * g.kswg * kBlockBytes;
   g.lds_asc = (size_t)p.mbw * g.ngw_max * 256;
   g.lds_red = p.wk > 1 ? (size_t)(p.wk - 1) * p.wn * p.mbw * p.ntw * 1024 : 0;
-  // raw bf16 rows of the fused stage; dead before the reduce area is used,
-  // so the two share one region
-  g.lds_raw = p.mode == 1 ? (size_t)p.mbw * 16 * g.kswg * 256 : 0;
-  g.lds_total = g.lds_a + g.lds_asc + (g.lds_red > g.lds_raw ? g.lds_red : g.lds_raw);
-  g.grid = (unsigned)((long long)g.mgroups * g.ngroups * p.split);
+  g.lds_total = g.lds_a + g.lds_asc + g.lds_red;
+  const long long tasks = (long long)g.ngroups * p.split;
+  g.grid = (unsigned)(8 * ((tasks + 7) / 8) * g.mgroups);
   g.threads = p.wn * p.wk * 64;
   return g;
 }
@@ -498,8 +531,7 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   args.kswg = geo.kswg;
   args.lds_asc_off = (unsigned)geo.lds_a;
   args.lds_red_off = (unsigned)(geo.lds_a + geo.lds_asc);
-  args.lds_raw_off = args.lds_red_off;
-  args.cpr_inv = (unsigned)((1ull << 32) / (16ull * geo.kswg) + 1);
+  args.kswg_inv = (1ull << 32) / (unsigned long long)geo.kswg + 1;
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(fn, dim3(geo.grid), dim3(geo.threads), kargs,
                                  (unsigned)geo.lds_total, stream);

@@ -22,6 +22,7 @@ struct Plan {
 };
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kAPT = 8;              // fused A items (16 bytes) per thread per load round
 constexpr int kMaxLastWgSplit = 16;  // split_k bound for the last-workgroup reduce
 constexpr int kMaxThreads = 512;
 
@@ -34,7 +35,6 @@ struct GemmGeom {
   size_t lds_a;    // bytes of A data in LDS
   size_t lds_asc;  // bytes of A scales in LDS
   size_t lds_red;  // bytes of the in-block reduce area
-  size_t lds_raw;  // bytes of raw bf16 A rows (fused mode)
   size_t lds_total;
   unsigned grid;
   int threads;

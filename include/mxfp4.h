@@ -99,9 +99,11 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
 /* ------------------------------------------------------------------------
  * GEMM plans.
  *
- * A plan fixes how one call is split over the GPU.  The grid has
- * ceil(ceil(M/16)/m_blocks) * ceil((N/16)/(waves_n*n_tiles_per_wave)) *
- * split_k workgroups of waves_n*waves_k wavefronts; each wavefront owns
+ * A plan fixes how one call is split over the GPU.  The work is
+ * ceil(ceil(M/16)/m_blocks) row groups times
+ * ceil((N/16)/(waves_n*n_tiles_per_wave)) * split_k column tasks, one
+ * workgroup of waves_n*waves_k wavefronts each (the row groups of one column
+ * task are placed on one XCD); each wavefront owns
  * n_tiles_per_wave 16-column tiles of B, m_blocks 16-row blocks of A, and
  * k_steps_per_wave 128-element K-steps.  The K steps must be covered
  * exactly: split_k * waves_k * k_steps_per_wave == K/128.  waves_k > 1 sums

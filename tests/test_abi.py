@@ -54,7 +54,13 @@ def test_packed_bytes_closed_form(lib):
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails first
 
+# The cases that pass fake device pointers must fail a host check before any
+# launch; as a second guard they only run where no GPU is present.
+no_gpu = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                            reason="fake-pointer error-path cases run only without a GPU")
 
+
+@no_gpu
 def test_gemm_rejects_bad_arguments(lib):
     f = lib.mxfp4_gemm
     nb = mx.packed_bytes(32, 512)
@@ -73,7 +79,31 @@ def test_gemm_rejects_bad_arguments(lib):
     assert f(FAKE, 512, FAKE, nb - 1, FAKE, 32, 4, 32, 512, None, 0, None) == ESIZE
 
 
-def test_gemm_rejects_bad_plans_and_workspace(lib):
+def test_plan_checks(lib):
+    M, N, K = 64, 256, 2048
+
+    def check(plan, m=M, n=N, k=K):
+        return lib.mxfp4_check_plan(ctypes.byref(plan._c()), m, n, k)
+
+    assert check(mx.Plan(mx.MODE_PREQUANT, 4, 1, 2, 1, 16, 1)) == 0
+    assert check(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
+    assert check(mx.Plan(1, 3, 1, 2, 1, 16, 1)) == ENOTSUP      # m_blocks
+    assert check(mx.Plan(1, 4, 1, 2, 1, 5, 1)) == ENOTSUP       # k_steps_per_wave
+    assert check(mx.Plan(1, 4, 1, 2, 1, 8, 1)) == EINVAL        # covers 8 of 16 steps
+    assert check(mx.Plan(1, 1, 1, 8, 2, 8, 1)) == EINVAL        # 16 wavefronts
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 0)) == 0         # reduce kernel: any split
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 1)) == 0         # last-WG reduce: split <= 16
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, 1), k=4096) == EINVAL
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, 0), k=4096) == 0
+    assert check(mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, 7)) == EINVAL  # split_reduce
+    # 64 rows x 128 K-steps of packed A per workgroup do not fit in LDS
+    assert check(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 8, 16, 1), k=16384) == EINVAL
+    assert "LDS" in mx.load().mxfp4_last_error().decode()
+    assert check(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 1, 16, 1)) == 0
+
+
+@no_gpu
+def test_gemm_rejects_bad_workspace(lib):
     f = lib.mxfp4_gemm_ex
     M, N, K = 64, 256, 2048
     nb = mx.packed_bytes(N, K)
@@ -88,31 +118,27 @@ def test_gemm_rejects_bad_plans_and_workspace(lib):
     assert call(good, None, 0) == ENULL                     # workspace required
     assert call(good, FAKE, need - 1) == EWORKSPACE
     assert call(good, ctypes.c_void_p(0x10010), need) == EINVAL  # 256-byte alignment
-    assert lib.mxfp4_check_plan(ctypes.byref(good._c()), M, N, K) == 0
-    assert call(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
-    assert call(mx.Plan(1, 3, 1, 2, 1, 16, 1)) == ENOTSUP      # m_blocks
-    assert call(mx.Plan(1, 4, 1, 2, 1, 5, 1)) == ENOTSUP       # k_steps_per_wave
-    assert call(mx.Plan(1, 4, 1, 2, 1, 8, 1)) == EINVAL        # covers 8 of 16 steps
-    assert call(mx.Plan(1, 1, 1, 8, 2, 8, 1)) == EINVAL        # 16 wavefronts
-    # fused stage of 64 rows x 2048 K in LDS does not fit
-    assert call(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 1, 16, 1)) == EINVAL
-    assert "LDS" in mx.load().mxfp4_last_error().decode()
-    # split-K: [tile counters][partials]; counters only for the last-WG reduce
+    assert call(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # an invalid plan is refused
+    split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
+    assert call(split, FAKE, 256 + 4 * M * N * 4 - 4) == EWORKSPACE
+
+
+def test_workspace_sizes(lib):
+    M, N, K = 64, 256, 2048
     split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
     tiles = 4 * 16  # (64/16)/1 row groups x (256/16)/1 column groups
     assert mx.workspace_zero_bytes(M, N, K, split) == 256 == -(-tiles * 4 // 256) * 256
     assert mx.workspace_bytes(M, N, K, split) == 256 + 4 * M * N * 4
-    assert call(split, FAKE, 256 + 4 * M * N * 4 - 4) == EWORKSPACE
     split_k = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_KERNEL)
     assert mx.workspace_zero_bytes(M, N, K, split_k) == 0
     assert mx.workspace_bytes(M, N, K, split_k) == 4 * M * N * 4
-    assert call(mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, 7)) == EINVAL  # split_reduce
     pq = mx.Plan(mx.MODE_PREQUANT, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
     assert mx.workspace_bytes(M, N, K, pq) == 256 + (mx.packed_bytes(M, K) + 255) // 256 * 256 \
         + 4 * M * N * 4
     assert mx.prequant_workspace_bytes(M, N, K, pq) == 256 + 4 * M * N * 4
 
 
+@no_gpu
 def test_quant_and_pack_reject_bad_arguments(lib):
     q = lib.mxfp4_quant_a
     assert q(None, 4, 512, 512, FAKE, 256, FAKE, 16, None) == ENULL
