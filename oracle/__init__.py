@@ -34,8 +34,9 @@ _i64 = ctypes.c_int64
 def _lib():
     global _LIB
     if _LIB is None:
-        path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        path = os.environ.get("MXFP4_ORACLE_LIB") or _build.LIB  # override: pin-strength test
+        if path == _build.LIB and (not os.path.exists(path)
+                                   or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
             _build.build()
         lib = ctypes.CDLL(path)
         lib.oracle_scale_byte.argtypes = [ctypes.c_float]

@@ -13,16 +13,18 @@ SRC = os.path.join(HERE, "mxfp4_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle; returns the library path."""
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(force: bool = True, out: str = LIB, mutant: int = 0) -> str:
+    """Compile the oracle; returns the library path.  `mutant` > 0 plants one
+    known mistake (for the test that checks the pins catch it)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+           "-ffp-contract=off", "-Wall", "-Wextra", "-DORACLE_MUTANT=%d" % mutant,
+           "-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
