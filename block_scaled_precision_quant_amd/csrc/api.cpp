@@ -64,8 +64,10 @@ mxfp4_plan make_plan(int mode, int mbw, int ntw, int wn, int wk, int ksw, int sp
 
 int check_gemm_shape(int M, int N, int K) {
   if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
-  if (N < 16 || N % 16 != 0) return fail(MXFP4_EINVAL, "N must be a positive multiple of 16 (got %d)", N);
-  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  if (N < 1) return fail(MXFP4_EINVAL, "N must be >= 1 (got %d)", N);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if ((long long)M * K > (1LL << 40) || (long long)N * K > (1LL << 40) || (long long)M * N > (1LL << 40))
+    return fail(MXFP4_EINVAL, "shape too large");
   return MXFP4_OK;
 }
 
@@ -88,9 +90,9 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
     return fail(MXFP4_ENOTSUP,
                 "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this build",
                 p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
-  const int KS = K / 128;
+  const int KS = (K + 127) / 128;
   if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
-    return fail(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal K/128)",
+    return fail(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal ceil(K/128))",
                 (long long)p.split_k * p.waves_k * p.k_steps_per_wave, KS);
   if (p.waves_n * p.waves_k > mx::kMaxThreads / 64)
     return fail(MXFP4_EINVAL, "plan has %d wavefronts per workgroup (max %d)", p.waves_n * p.waves_k,
@@ -148,7 +150,7 @@ mxfp4_plan default_plan(int M, int N, int K) {
   // Heuristic: fused quantization for small M, prequant otherwise; the
   // largest compiled per-wave step count that divides K/128 with at most 8
   // workgroups along K; in-block split along K when the grid is thin.
-  const int KS = K / 128;
+  const int KS = (K + 127) / 128;
   const int MT = (M + 15) / 16;
   const int mode = M <= 32 ? MXFP4_MODE_FUSED : MXFP4_MODE_PREQUANT;
   const int mbw = MT >= 4 ? 4 : (MT >= 2 ? 2 : 1);
@@ -206,7 +208,7 @@ int check_stream_ptrs(const void* p, const char* name) {
 extern "C" {
 
 size_t mxfp4_packed_bytes(int rows, int K) {
-  if (rows < 1 || K < 128 || K % 128 != 0) return 0;
+  if (rows < 1 || K < 32 || K % 32 != 0) return 0;
   return mx::packed_dims(rows, K).total_bytes();
 }
 
@@ -216,8 +218,8 @@ int mxfp4_pack_b(const uint8_t* b_fp4, const uint8_t* b_scale, int N, int K, voi
   if ((rc = check_stream_ptrs(b_fp4, "b_fp4")) || (rc = check_stream_ptrs(b_scale, "b_scale")) ||
       (rc = check_stream_ptrs(b_packed, "b_packed")))
     return rc;
-  if (N < 16 || N % 16 != 0) return fail(MXFP4_EINVAL, "N must be a positive multiple of 16 (got %d)", N);
-  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  if (N < 1) return fail(MXFP4_EINVAL, "N must be >= 1 (got %d)", N);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
   if (!aligned(b_fp4, 16) || !aligned(b_packed, 16))
     return fail(MXFP4_EINVAL, "b_fp4 and b_packed must be 16-byte aligned");
   const size_t need = mxfp4_packed_bytes(N, K);
@@ -258,7 +260,7 @@ int mxfp4_quant_a_packed(const uint16_t* a, int M, int K, int lda, void* out_pac
   if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(out_packed, "out_packed")))
     return rc;
   if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
-  if (K < 128 || K % 128 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 128 (got %d)", K);
+  if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
   if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
   if (!aligned(a, 16) || !aligned(out_packed, 16))
     return fail(MXFP4_EINVAL, "a and out_packed must be 16-byte aligned");

@@ -106,10 +106,14 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   uint8_t* lds_sc = smem + g.lds_asc_off;
   const int rows_valid = min(MBW * 16, g.M - m0);
   const int n_items = MODE == 1 ? ((rows_valid + 15) >> 4) * kswg * 256 : 0;
+  // valid: the item has an LDS slot to fill (a row < M); inside: its group
+  // lies below K (else it is quantized as zeros).  Both are uniform over a
+  // quad (same row, same group).
   struct Item {
     int r, jl, kg, p;
-    bool valid;
+    bool valid, inside;
   };
+  const int groups = g.K / kGroup;
   auto item = [&](int it) {
     Item x;
     x.p = it & 3;
@@ -119,14 +123,17 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
     const int rg = (int)(((unsigned long long)rest * g.kswg_inv) >> 32);
     x.jl = rest - rg * kswg;
     x.r = rg * 16 + r16;
-    x.valid = it < n_items && x.r < rows_valid;  // uniform over a quad (same row)
+    x.valid = it < n_items && x.r < rows_valid;
+    x.inside = x.valid && (jw0 + x.jl) * 4 + x.kg < groups;
     return x;
   };
-  auto item_ptr = [&](const Item& x) {
-    const int r = x.valid ? x.r : 0;
-    const size_t col = x.valid ? ((size_t)(jw0 + x.jl) * kStep + x.kg * 32 + x.p * 8)
-                               : (size_t)jw0 * kStep;
-    return reinterpret_cast<const uint4*>(g.a + (size_t)(m0 + r) * g.lda + col);
+  // unused items read the workgroup's first element (always in bounds)
+  auto load_item = [&](const Item& x) {
+    const int r = x.inside ? x.r : 0;
+    const size_t col = x.inside ? ((size_t)(jw0 + x.jl) * kStep + x.kg * 32 + x.p * 8)
+                                : (size_t)jw0 * kStep;
+    const uint4 v = *reinterpret_cast<const uint4*>(g.a + (size_t)(m0 + r) * g.lda + col);
+    return v;
   };
   auto quantize_item = [&](const Item& x, uint4 v) {
     const int jj = jw0 + x.jl;
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   uint4 araw[kAPT];
   if constexpr (MODE == 1) {
 #pragma unroll
-    for (int u = 0; u < kAPT; ++u) araw[u] = *item_ptr(item(tid + u * nthreads));
+    for (int u = 0; u < kAPT; ++u) araw[u] = load_item(item(tid + u * nthreads));
   } else {
     const PackedDims da = {g.MT, g.KS, g.KG};
     const int mbv = min(MBW, g.MT - mg * MBW);
@@ -185,19 +192,20 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   }
 
   if constexpr (MODE == 1) {
+    const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < kAPT; ++u) {
       const Item x = item(tid + u * nthreads);
-      if (x.valid) quantize_item(x, araw[u]);
+      if (x.valid) quantize_item(x, x.inside ? araw[u] : zero);
     }
     // further rounds (plans whose A stage exceeds kAPT items per thread)
     for (int base = kAPT * nthreads; base < n_items; base += kAPT * nthreads) {
 #pragma unroll
-      for (int u = 0; u < kAPT; ++u) araw[u] = *item_ptr(item(base + tid + u * nthreads));
+      for (int u = 0; u < kAPT; ++u) araw[u] = load_item(item(base + tid + u * nthreads));
 #pragma unroll
       for (int u = 0; u < kAPT; ++u) {
         const Item x = item(base + tid + u * nthreads);
-        if (x.valid) quantize_item(x, araw[u]);
+        if (x.valid) quantize_item(x, x.inside ? araw[u] : zero);
       }
     }
   } else {
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
-          if (row >= g.M) continue;
+          if (row >= g.M || col >= g.N) continue;
           float* part = g.ws + ((size_t)s * g.M + row) * g.N + col;
           if (g.split == 1)
             g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[b][i][e]);
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = min(m0 + b * 16 + 4 * (lane >> 4) + e, g.M - 1);
-          float* src = g.ws + (size_t)row * g.N + col;
+          float* src = g.ws + (size_t)row * g.N + min(col, g.N - 1);
 #pragma unroll
           for (int k = 0; k < kMaxLastWgSplit; ++k)
             if (k < g.split)
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int k = 1; k < kMaxLastWgSplit; ++k)
             if (k < g.split) sum += v[e][k];
-          if (row < g.M) g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(sum);
+          if (row < g.M && col < g.N) g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(sum);
         }
       }
     }
@@ -387,16 +395,27 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 }
 
 // Sum split fp32 partials [S][M][N] in order s = 0..S-1 and round to bf16.
-// One thread per 4 consecutive outputs (N % 16 == 0).
+// With N % 4 == 0 one thread takes 4 consecutive outputs (16-byte loads);
+// otherwise one output.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             uint16_t* __restrict__ c, int M,
                                                             int N, int ldc, int S) {
-  const int n4 = N / 4;
+  const size_t plane = (size_t)M * N;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((N & 3) != 0) {
+    if (idx >= (long long)plane) return;
+    const int row = (int)(idx / N);
+    const int col = (int)(idx % N);
+    const float* src = ws + idx;
+    float acc = src[0];
+    for (int k = 1; k < S; ++k) acc += src[(size_t)k * plane];
+    c[(size_t)row * ldc + col] = f32_to_bf16_rne(acc);
+    return;
+  }
+  const int n4 = N / 4;
   if (idx >= (long long)M * n4) return;
   const int row = (int)(idx / n4);
   const int col = (int)(idx % n4) * 4;
-  const size_t plane = (size_t)M * N;
   const float* src = ws + (size_t)row * N + col;
   float4 acc = *reinterpret_cast<const float4*>(src);
   for (int k = 1; k < S; ++k) {
@@ -475,10 +494,11 @@ bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw) {
 
 GemmGeom gemm_geometry(const Plan& p, int M, int N, int K) {
   GemmGeom g;
+  const PackedDims bd = packed_dims(N, K);
   g.MT = (M + 15) / 16;
-  g.NT = N / 16;
-  g.KS = K / kStep;
-  g.KG = (g.KS + 3) / 4;
+  g.NT = bd.RT;
+  g.KS = bd.KS;
+  g.KG = bd.KG;
   g.mgroups = (g.MT + p.mbw - 1) / p.mbw;
   const int cols_per_wg = p.wn * p.ntw;
   g.ngroups = (g.NT + cols_per_wg - 1) / cols_per_wg;
@@ -537,7 +557,7 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
                                  (unsigned)geo.lds_total, stream);
   if (e != hipSuccess) return e;
   if (p.split > 1 && !p.last_wg) {
-    const long long n = (long long)M * (N / 4);
+    const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
     const unsigned grid = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, M, N, ldc,
                        p.split);

@@ -32,10 +32,12 @@ struct PackedDims {
   }
 };
 
+// K is padded up to whole 128-element steps; the padding holds code 0 and
+// scale 127 (a zero contribution).
 __host__ __device__ inline PackedDims packed_dims(int rows, int K) {
   PackedDims d;
   d.RT = (rows + kTileRows - 1) / kTileRows;
-  d.KS = K / kStep;
+  d.KS = (K + kStep - 1) / kStep;
   d.KG = (d.KS + 3) / 4;
   return d;
 }

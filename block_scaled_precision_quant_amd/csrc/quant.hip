@@ -32,12 +32,14 @@ __global__ __launch_bounds__(256) void quant_linear_kernel(const uint16_t* __res
   if ((kk & 3) == 0) out_scale[(size_t)row * ld_scale + (kk >> 2)] = (uint8_t)byte;
 }
 
-// MX-packed output, padding rows included (code 0, scale 127).
+// MX-packed output, padding included: rows >= M and K-groups >= K/32 get
+// code 0 and scale 127.  One thread per 8-element item of the padded
+// RT*16 x KS*128 matrix.
 __global__ __launch_bounds__(256) void quant_packed_kernel(const uint16_t* __restrict__ a, int M,
                                                            int K, int lda,
                                                            uint8_t* __restrict__ out,
                                                            PackedDims d) {
-  const int per_row = K / 8;
+  const int per_row = d.KS * 16;  // 8-element items per padded row
   const long long n_items = (long long)d.RT * kTileRows * per_row;
   const long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (it >= n_items) return;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void quant_packed_kernel(const uint16_t* __res
   const int lane = (row & 15) + 16 * (gi & 3);
   const int t = row >> 4;
   uint32_t codes = 0, byte = 127;
-  if (row < M) {  // uniform over the quad (same row)
+  if (row < M && gi < K / kGroup) {  // uniform over the quad (same row and group)
     const uint4 v = *reinterpret_cast<const uint4*>(a + (size_t)row * lda + (size_t)kk * 8);
     const uint32_t amax = quad_max(amax8_bits(v));
     byte = scale_byte_from_amax(amax);
@@ -67,13 +69,15 @@ __global__ __launch_bounds__(256) void quant_packed_kernel(const uint16_t* __res
 
 // One-time repack of linear fp4 [N][K/2] + e8m0 [N][K/32] into MX-packed.
 // Threads [0, RT*KS*64) move one 16-byte data chunk each; threads
-// [RT*KS*64, RT*KS*64 + RT*KG*64) assemble one scale dword each.
+// [RT*KS*64, RT*KS*64 + RT*KG*64) assemble one scale dword each.  Rows >= N
+// and K beyond K get code 0 and scale 127.
 __global__ __launch_bounds__(256) void pack_b_kernel(const uint8_t* __restrict__ b_fp4,
                                                      const uint8_t* __restrict__ b_scale, int N,
                                                      int K, uint8_t* __restrict__ out,
                                                      PackedDims d) {
   const long long n_data = (long long)d.RT * d.KS * 64;
   const long long n_scale = (long long)d.RT * d.KG * 64;
+  const int groups = K / kGroup;
   long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (it < n_data) {
     const int lane = (int)(it & 63);
@@ -81,8 +85,10 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const uint8_t* __restrict__
     const int j = (int)(tj % d.KS);
     const int t = (int)(tj / d.KS);
     const int row = 16 * t + (lane & 15);
-    const uint4 v = *reinterpret_cast<const uint4*>(b_fp4 + (size_t)row * (K / 2) +
-                                                    (size_t)(64 * j + 16 * (lane >> 4)));
+    const int g = 4 * j + (lane >> 4);  // the 32-group this lane's 16 bytes hold
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (row < N && g < groups)
+      v = *reinterpret_cast<const uint4*>(b_fp4 + (size_t)row * (K / 2) + (size_t)g * 16);
     *reinterpret_cast<uint4*>(out + d.data_off(t, j, lane)) = v;
     return;
   }
@@ -90,17 +96,17 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const uint8_t* __restrict__
   if (it >= n_scale) return;
   const int lane = (int)(it & 63);
   const long long tg = it >> 6;
-  const int g = (int)(tg % d.KG);
+  const int g4 = (int)(tg % d.KG);
   const int t = (int)(tg / d.KG);
   const int row = 16 * t + (lane & 15);
   uint32_t word = 0;
   for (int s = 0; s < 4; ++s) {
-    const int j = 4 * g + s;
+    const int grp = 4 * (4 * g4 + s) + (lane >> 4);
     const uint32_t byte =
-        j < d.KS ? b_scale[(size_t)row * (K / 32) + 4 * j + (lane >> 4)] : 127u;
+        (row < N && grp < groups) ? b_scale[(size_t)row * groups + grp] : 127u;
     word |= byte << (8 * s);
   }
-  *reinterpret_cast<uint32_t*>(out + d.scale_off(t, g, lane)) = word;
+  *reinterpret_cast<uint32_t*>(out + d.scale_off(t, g4, lane)) = word;
 }
 
 // --------------------------------------------------------------- launchers
@@ -119,7 +125,7 @@ void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_
 void launch_quant_packed(const uint16_t* a, int M, int K, int lda, uint8_t* out,
                          hipStream_t stream) {
   const PackedDims d = packed_dims(M, K);
-  const long long n = (long long)d.RT * kTileRows * (K / 8);
+  const long long n = (long long)d.RT * kTileRows * d.KS * 16;
   hipLaunchKernelGGL(quant_packed_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, a, M, K,
                      lda, out, d);
 }

@@ -53,27 +53,29 @@ extern "C" {
  * Both the pre-packed B and the pre-quantized A use one layout, laid out in
  * the lane order of the gfx950 block-scaled 16x16x128 FP4 matrix instruction
  * (lane L holds row L%16 and the 32-element K-group L/16 of a 128-K step).
- * For a matrix of R rows and K columns (K % 128 == 0):
- *     RT = ceil(R/16) row tiles, KS = K/128 steps, KG = ceil(KS/4),
+ * For a matrix of R rows and K columns (K % 32 == 0; K is padded up to whole
+ * 128-element steps):
+ *     RT = ceil(R/16) row tiles, KS = ceil(K/128) steps, KG = ceil(KS/4),
  *     data bytes  D = RT*KS*1024,  total bytes = D + RT*KG*256.
  *   data:  byte ((t*KS + j)*64 + L)*16 + i  holds linear fp4x2 byte
  *          (64*j + 16*(L/16) + i) of row 16*t + L%16,  i in [0,16);
  *   scale: byte D + ((t*KG + g)*64 + L)*4 + s  holds the e8m0 scale of row
  *          16*t + L%16, K-group 4*(4*g + s) + L/16, for step 4*g+s < KS;
  *          bytes for steps >= KS hold 127.
- * Rows >= R (padding of the last tile) hold code 0 and scale 127.
+ * Padding -- rows >= R, and K-groups at or beyond K/32 -- holds code 0 and
+ * scale 127 (a zero contribution to any product).
  * ---------------------------------------------------------------------- */
 
 /* Bytes of the MX-packed layout for `rows` rows of K columns; 0 when
- * rows < 1 or K is not a positive multiple of 128. */
+ * rows < 1 or K is not a positive multiple of 32. */
 size_t mxfp4_packed_bytes(int rows, int K);
 
 /* One-time repack of a quantized B into the MX-packed layout.
  *   b_fp4   [N][K/2]  fp4x2, row-major, contiguous (16-byte aligned);
  *   b_scale [N][K/32] e8m0,  row-major, contiguous;
  *   b_packed  output, mxfp4_packed_bytes(N, K) bytes, 16-byte aligned.
- * Requires N % 16 == 0, N >= 16, K % 128 == 0, K >= 128.  This is a byte
- * permutation only (no arithmetic).  Errors: ENULL, EINVAL, ESIZE, EHIP. */
+ * Requires N >= 1, K >= 32, K % 32 == 0.  This is a byte permutation only
+ * (no arithmetic).  Errors: ENULL, EINVAL, ESIZE, EHIP. */
 int mxfp4_pack_b(const uint8_t *b_fp4, const uint8_t *b_scale, int N, int K, void *b_packed,
                  size_t b_packed_bytes, void *stream);
 
@@ -92,7 +94,10 @@ int mxfp4_quant_a(const uint16_t *a, int M, int K, int lda, uint8_t *out_fp4, in
 /* Quantize bf16 rows straight into the MX-packed layout (the layout the
  * GEMM reads), padding rows included.
  *   a  as for mxfp4_quant_a;  out_packed  mxfp4_packed_bytes(M, K) bytes,
- *   16-byte aligned.  Requires K % 128 == 0.  Errors: ENULL, EINVAL, ESIZE, EHIP. */
+ *   16-byte aligned.  Requires M >= 1, K >= 32, K % 32 == 0.  Applied to a
+ *   weight matrix B [N][K] this is the one-time B preparation straight from
+ *   bf16 (the same bytes as mxfp4_quant_a followed by mxfp4_pack_b).
+ *   Errors: ENULL, EINVAL, ESIZE, EHIP. */
 int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_packed,
                          size_t out_packed_bytes, void *stream);
 
@@ -106,7 +111,7 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * task are placed on one XCD); each wavefront owns
  * n_tiles_per_wave 16-column tiles of B, m_blocks 16-row blocks of A, and
  * k_steps_per_wave 128-element K-steps.  The K steps must be covered
- * exactly: split_k * waves_k * k_steps_per_wave == K/128.  waves_k > 1 sums
+ * exactly: split_k * waves_k * k_steps_per_wave == ceil(K/128).  waves_k > 1 sums
  * the wavefronts' partial tiles in LDS (fixed order); split_k > 1 writes fp32
  * partials [split_k][M][N] to the workspace and sums them in order
  * s = 0..split_k-1, rounding to bf16 (nearest even) -- either in a separate
@@ -173,7 +178,7 @@ size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
  *             bytes, 256-byte aligned (may be NULL when that is 0), whose
  *             leading zero-bytes (see mxfp4_plan_workspace_zero_bytes) were
  *             zero-filled once before first use.
- * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ * Requires M >= 1, N >= 1, K >= 32, K % 32 == 0.
  * Inputs are finite.  Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
 int mxfp4_gemm(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
                uint16_t *c, int ldc, int M, int N, int K, void *workspace,

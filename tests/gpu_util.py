@@ -26,22 +26,21 @@ def bf16_out_to_f32(c):
 
 def packed_dims(rows, K):
     RT = -(-rows // 16)
-    KS = K // 128
+    KS = -(-K // 128)
     KG = -(-KS // 4)
     return RT, KS, KG
 
 
 def pack_host(fp4, scale):
-    """Linear fp4x2 [R, K/2] + e8m0 [R, K/32] -> MX-packed bytes (padding rows:
-    code 0, scale 127; scale bytes of steps >= KS: 127)."""
+    """Linear fp4x2 [R, K/2] + e8m0 [R, K/32] -> MX-packed bytes (padding rows
+    and K-groups past K: code 0, scale 127; scale bytes of steps >= KS: 127)."""
     R, half = fp4.shape
     K = 2 * half
     RT, KS, KG = packed_dims(R, K)
-    q = np.zeros((RT * 16, half), dtype=np.uint8)
-    q[:R] = fp4
+    q = np.zeros((RT * 16, KS * 64), dtype=np.uint8)
+    q[:R, :half] = fp4
     s = np.full((RT * 16, KG * 16), 127, dtype=np.uint8)
     s[:R, :K // 32] = scale
-    s[R:, :] = 127
     # data[t, j, h, r, i] = q[16t + r, 64j + 16h + i]
     data = q.reshape(RT, 16, KS, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
     # sc[t, g, h, r, s] = scale[16t + r, 4*(4g + s) + h]
@@ -57,7 +56,7 @@ def unpack_host(buf, R, K):
     q = data.transpose(0, 3, 1, 2, 4).reshape(RT * 16, KS * 64)
     sc = np.asarray(buf[D:D + RT * KG * 256], dtype=np.uint8).reshape(RT, KG, 4, 16, 4)
     s = sc.transpose(0, 3, 1, 4, 2).reshape(RT * 16, KG * 16)
-    return q[:R], s[:R, :K // 32]
+    return q[:R, :K // 2], s[:R, :K // 32]
 
 
 def assert_close_to_oracle(got, want, label=""):

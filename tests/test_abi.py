@@ -43,13 +43,15 @@ def test_version(lib):
 
 
 def test_packed_bytes_closed_form(lib):
-    for rows, K in [(16, 128), (4, 512), (2880, 512), (2112, 7168), (17, 640), (256, 1536)]:
-        RT, KS = -(-rows // 16), K // 128
+    for rows, K in [(16, 128), (4, 512), (2880, 512), (2112, 7168), (17, 640), (256, 1536),
+                    (5, 32), (33, 96), (7, 544)]:
+        RT, KS = -(-rows // 16), -(-K // 128)
         KG = -(-KS // 4)
         assert mx.packed_bytes(rows, K) == RT * KS * 1024 + RT * KG * 256
     # B's layout is exactly N*K/2 + N*K/32 bytes when K % 512 == 0
     assert mx.packed_bytes(2880, 512) == 2880 * 256 + 2880 * 16
     assert mx.packed_bytes(0, 512) == 0 and mx.packed_bytes(16, 100) == 0
+    assert mx.packed_bytes(16, 0) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails first
@@ -68,8 +70,8 @@ def test_gemm_rejects_bad_arguments(lib):
     assert f(FAKE, 512, None, nb, FAKE, 32, 4, 32, 512, None, 0, None) == ENULL
     assert f(FAKE, 512, FAKE, nb, None, 32, 4, 32, 512, None, 0, None) == ENULL
     assert f(FAKE, 512, FAKE, nb, FAKE, 32, 0, 32, 512, None, 0, None) == EINVAL  # M
-    assert f(FAKE, 512, FAKE, nb, FAKE, 40, 4, 40, 512, None, 0, None) == EINVAL  # N % 16
-    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 32, 500, None, 0, None) == EINVAL  # K % 128
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 0, 512, None, 0, None) == EINVAL   # N
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 32, 500, None, 0, None) == EINVAL  # K % 32
     assert f(FAKE, 256, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda < K
     assert f(FAKE, 516, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda % 8
     assert f(FAKE, 512, FAKE, nb, FAKE, 16, 4, 32, 512, None, 0, None) == EINVAL  # ldc < N
@@ -148,9 +150,9 @@ def test_quant_and_pack_reject_bad_arguments(lib):
     assert q(FAKE, 4, 512, 512, FAKE, 256, FAKE, 8, None) == EINVAL   # ld_scale < K/32
     qp = lib.mxfp4_quant_a_packed
     assert qp(FAKE, 4, 512, 512, FAKE, mx.packed_bytes(4, 512) - 1, None) == ESIZE
-    assert qp(FAKE, 4, 96, 96, FAKE, 1 << 20, None) == EINVAL         # K % 128
+    assert qp(FAKE, 4, 100, 104, FAKE, 1 << 20, None) == EINVAL       # K % 32
     pb = lib.mxfp4_pack_b
-    assert pb(FAKE, FAKE, 24, 512, FAKE, 1 << 20, None) == EINVAL     # N % 16
+    assert pb(FAKE, FAKE, 0, 512, FAKE, 1 << 20, None) == EINVAL      # N
     assert pb(FAKE, FAKE, 32, 512, FAKE, mx.packed_bytes(32, 512) - 1, None) == ESIZE
     assert pb(FAKE, None, 32, 512, FAKE, 1 << 20, None) == ENULL
 
@@ -159,11 +161,12 @@ def test_default_plans_are_valid(lib):
     from block_scaled_precision_quant_amd import inputs
     shapes = [(w.M, w.N, w.K) for w in inputs.WORKLOADS.values()]
     shapes += [(8, 2112, 7168), (16, 3072, 1536), (64, 3072, 1536), (256, 2880, 512),
-               (1, 16, 128), (100, 1008, 1152), (33, 528, 640)]
+               (1, 16, 128), (100, 1008, 1152), (33, 528, 640), (1, 1, 32), (5, 24, 96),
+               (70, 100, 544), (3, 4100, 8192)]
     for M, N, K in shapes:
         p = mx.default_plan(M, N, K)
         mx.check_plan(p, M, N, K)
-        assert p.split_k * p.waves_k * p.k_steps_per_wave == K // 128, (M, N, K, p)
+        assert p.split_k * p.waves_k * p.k_steps_per_wave == -(-K // 128), (M, N, K, p)
         # a valid plan has a well-defined workspace size (0 only if none needed)
         ws = mx.workspace_bytes(M, N, K, p)
         if p.mode == mx.MODE_PREQUANT or p.split_k > 1:

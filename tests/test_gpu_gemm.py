@@ -110,7 +110,10 @@ def test_workload_plan_override(name, plan):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 48, 256), (17, 80, 384), (33, 144, 640),
-                                   (100, 1008, 1152), (63, 272, 896), (2, 16, 7168)])
+                                   (100, 1008, 1152), (63, 272, 896), (2, 16, 7168),
+                                   # general shapes: N not a multiple of 16, K of 32
+                                   (1, 1, 32), (5, 24, 96), (3, 40, 160), (17, 100, 544),
+                                   (70, 100, 544), (33, 1000, 1504), (9, 17, 4128)])
 def test_ragged_shapes_default_plan(M, N, K):
     print("case", M, N, K, mx.default_plan(M, N, K), flush=True)
     ref = reference((M, N, K, M * 7 + N))
@@ -127,6 +130,28 @@ def test_ragged_shapes_default_plan(M, N, K):
 def test_ragged_shapes_plans(M, N, K, plan):
     print("case", M, N, K, plan, flush=True)
     ref = reference((M, N, K, 99 + M))
+    assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "%dx%dx%d %s" % (M, N, K, plan))
+
+
+# the pages' correctness shapes (submission 752099's configuration table)
+@pytest.mark.parametrize("M,N,K", [(8, 2112, 7168), (16, 3072, 1536), (64, 3072, 1536),
+                                   (256, 2880, 512)])
+def test_page_test_shapes(M, N, K):
+    print("case", M, N, K, mx.default_plan(M, N, K), flush=True)
+    ref = reference((M, N, K, M + N + K))
+    assert_close_to_oracle(run_gemm(ref), ref["c32"], "%dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K,plan", [
+    (17, 100, 544, mx.Plan(F, 1, 1, 2, 1, 1, 5, 0)),
+    (17, 100, 544, mx.Plan(P, 2, 2, 1, 1, 1, 5, 1)),
+    (5, 24, 96, mx.Plan(F, 1, 2, 1, 1, 1, 1)),
+    (33, 1000, 1504, mx.Plan(F, 2, 1, 2, 3, 4, 1)),
+    (33, 1000, 1504, mx.Plan(P, 1, 2, 2, 1, 3, 4, 1)),
+])
+def test_general_shapes_plans(M, N, K, plan):
+    print("case", M, N, K, plan, flush=True)
+    ref = reference((M, N, K, 7 + M))
     assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "%dx%dx%d %s" % (M, N, K, plan))
 
 

@@ -89,7 +89,8 @@ def test_quant_a_special_groups():
     assert np.array_equal(q2.cpu().numpy(), rq) and np.array_equal(s2.cpu().numpy(), rs)
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (4, 512), (17, 640), (64, 2048), (16, 7168)])
+@pytest.mark.parametrize("M,K", [(1, 128), (4, 512), (17, 640), (64, 2048), (16, 7168),
+                                 (5, 96), (17, 544), (1, 32)])
 def test_quant_a_packed_layout(M, K):
     a, _ = inputs.make_shape(M, 16, K, seed=M + K)
     rq, rs = oracle.quantize(a)
@@ -101,7 +102,8 @@ def test_quant_a_packed_layout(M, K):
     assert np.array_equal(q, rq) and np.array_equal(s, rs)
 
 
-@pytest.mark.parametrize("N,K", [(16, 128), (2880, 512), (2112, 7168), (48, 640)])
+@pytest.mark.parametrize("N,K", [(16, 128), (2880, 512), (2112, 7168), (48, 640),
+                                 (24, 96), (1, 32), (100, 544)])
 def test_pack_b_layout(N, K):
     _, b = inputs.make_shape(4, N, K, seed=N)
     rq, rs = oracle.quantize(b)
@@ -110,3 +112,14 @@ def test_pack_b_layout(N, K):
     got = buf.cpu().numpy()
     assert got.size == mx.packed_bytes(N, K)
     assert np.array_equal(got, pack_host(rq, rs))
+
+
+@pytest.mark.parametrize("N,K", [(2880, 512), (100, 544), (7, 32)])
+def test_b_prepared_from_bf16(N, K):
+    """The one-time B preparation straight from bf16 (the packed quantizer
+    applied to B) gives the bytes of the oracle's B, packed."""
+    _, b = inputs.make_shape(1, N, K, seed=N + 3)
+    rq, rs = oracle.quantize(b)
+    buf = mx.quant_a_packed(to_dev_bf16(b))
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), pack_host(rq, rs))
