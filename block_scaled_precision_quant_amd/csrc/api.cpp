@@ -147,45 +147,37 @@ mxfp4_plan default_plan(int M, int N, int K) {
   for (const Row& r : table)
     if (r.M == M && r.N == N && r.K == K) return r.p;
 
-  // Heuristic: fused quantization for small M, prequant otherwise; the
-  // largest compiled per-wave step count that divides K/128 with at most 8
-  // workgroups along K; in-block split along K when the grid is thin.
+  // Heuristic, from the sweeps over the tuned shapes: fused quantization,
+  // one 16-row block per workgroup (row groups of one column task share B in
+  // one XCD's L2), four wavefronts along N, the largest compiled step count
+  // per wavefront that divides the K steps (at most 16), then up to two
+  // wavefronts along K inside the workgroup and the rest as workgroups along
+  // K summed by the reduce kernel.
   const int KS = (K + 127) / 128;
-  const int MT = (M + 15) / 16;
-  const int mode = M <= 32 ? MXFP4_MODE_FUSED : MXFP4_MODE_PREQUANT;
-  const int mbw = MT >= 4 ? 4 : (MT >= 2 ? 2 : 1);
+  const int NT = (N + 15) / 16;
   static const int ksw_opts[] = {16, 14, 12, 8, 7, 6, 4, 3, 2, 1};
   int ksw = 1;
   for (int k : ksw_opts)
-    if (KS % k == 0 && KS / k <= 8) {
+    if (KS % k == 0) {
       ksw = k;
       break;
     }
-  if (KS % ksw != 0 || KS / ksw > 8) {
-    for (int k : ksw_opts)
-      if (KS % k == 0) {
-        ksw = k;
-        break;
-      }
+  const int rest = KS / ksw;  // split_k * waves_k
+  int wn = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
+  int wk = (rest % 2 == 0) ? 2 : 1;
+  // a grid already wide without K splits keeps K inside the workgroup
+  const long long wide = (long long)((M + 15) / 16) * ((NT + wn - 1) / wn);
+  if (wide >= 512 && rest > 1) {
+    wn = 2;
+    wk = 1;
+    while (wk < 4 && rest % (wk * 2) == 0) wk *= 2;
   }
-  int rest = KS / ksw;  // split_k * waves_k
-  int wk = 1;
-  while (wk < 4 && rest % (wk * 2) == 0) wk *= 2;
-  mxfp4_plan p = make_plan(mode, mbw, 1, 2, wk, ksw, rest / wk);
-  // keep the workgroup's A stage within LDS: trade in-block K waves for
-  // workgroups along K, then smaller row blocks, then the prequant stage
-  for (;;) {
-    if (mx::gemm_geometry(to_internal(p), M, N, K).lds_total <= (size_t)mx::kMaxLds) break;
-    if (p.waves_k > 1) {
-      p.waves_k /= 2;
-      p.split_k *= 2;
-    } else if (p.m_blocks > 1) {
-      p.m_blocks /= 2;
-    } else if (p.mode == MXFP4_MODE_FUSED) {
-      p.mode = MXFP4_MODE_PREQUANT;
-    } else {
-      break;
-    }
+  mxfp4_plan p = make_plan(MXFP4_MODE_FUSED, 1, 1, wn, wk, ksw, rest / wk);
+  // keep the A stage within LDS: trade in-block K waves for workgroups along K
+  while (mx::gemm_geometry(to_internal(p), M, N, K).lds_total > (size_t)mx::kMaxLds &&
+         p.waves_k > 1) {
+    p.waves_k /= 2;
+    p.split_k *= 2;
   }
   return p;
 }
