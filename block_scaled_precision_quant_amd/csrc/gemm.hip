@@ -5,15 +5,16 @@
 //   rows    [m0, m0 + 16*MBW)            MBW blocks of the MFMA's 16 rows
 //   columns wn wavefronts x NTW tiles of 16 columns
 //   K       wk wavefronts x KSW steps of 128, starting at step jw0
-// Each wavefront streams its own B tiles straight from HBM into registers
-// (16 bytes per lane per step, one coalesced 1 KiB block per load
-// instruction), issuing all of them before touching A so that the B
-// latency overlaps the A stage.  The workgroup's A rows for its K range are
-// staged once in LDS in the instruction's lane order -- quantized in the
-// kernel from bf16 (fused mode) or copied from the MX-packed A (prequant
-// mode) -- and every wavefront reads its A operand from there.  Partial tiles
-// of the wk wavefronts are summed in LDS in a fixed order; with split > 1 the
-// workgroup writes an fp32 partial and splitk_reduce_kernel sums them.
+// The workgroup's A rows for its K range are staged once in LDS in the
+// instruction's lane order -- quantized in the kernel from bf16 (fused
+// mode) or copied from the MX-packed A (prequant mode) -- and every
+// wavefront reads its A operand from there.  Each wavefront streams its own
+// B tiles straight from HBM into registers (16 bytes per lane per step, one
+// coalesced 1 KiB block per load instruction); its A loads go first, so the
+// A quantization overlaps the B loads' latency.  Partial tiles of the wk
+// wavefronts are summed in LDS in a fixed order; with split > 1 the
+// workgroup writes an fp32 partial, summed by splitk_reduce_kernel or by the
+// last workgroup of the tile.
 #include <atomic>
 
 #include "mx_internal.hpp"
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform, so everything derived from it lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_n = wave % g.wn;
   const int wave_k = wave / g.wn;
   const int nthreads = blockDim.x;
@@ -88,69 +90,79 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   const int ngw = ((jw0 + kswg - 1) >> 2) - gw0 + 1;
   const int nt_base = (ng * g.wn + wave_n) * NTW;
 
-  // ---- 1. A for steps [jw0, jw0 + kswg).  Fused mode: the first kAPT raw
-  //         items of every thread are loaded into registers before any B
-  //         load is issued (addresses of unused items are clamped to a valid
-  //         one, so the number of load instructions is fixed and the
-  //         compiler's wait for them leaves the B loads in flight while A is
-  //         quantized).  Prequant mode: the packed A blocks are copied to LDS
-  //         by LDS-direct loads (global -> LDS without registers).
+  // ---- 1. A for steps [jw0, jw0 + kswg).  Fused mode: the first kAPT
+  //         chunks of every wavefront are loaded into registers before any B
+  //         load is issued (rows past M and chunks past K read the
+  //         workgroup's first elements instead, so the number of load
+  //         instructions is fixed and the compiler's wait for them leaves the
+  //         B loads in flight while A is quantized).  Prequant mode: the
+  //         packed A blocks are copied to LDS by LDS-direct loads (global ->
+  //         LDS without registers).
   //
-  //         A fused item is 8 consecutive bf16 (16 bytes); the 4 items of an
-  //         aligned quad of lanes form one 32-element group, and a
-  //         wavefront's 64 items are 16 rows x 4 quarters of one (step,
-  //         K-group) -- 16 rows x 64 contiguous bytes in global memory and
-  //         64 consecutive LDS words for its codes (no bank conflicts).
+  //         Fused A is handled per (row block rg, step jl), numbered
+  //         rest = rg*kswg + jl: 16 rows x 128 elements, i.e. four chunks, one
+  //         per K-group kg.  In a chunk lane L takes row L/4 and quarter L%4
+  //         (8 consecutive bf16, 16 bytes), so an aligned quad of lanes holds
+  //         one 32-element group, and the chunk's 64 code dwords fill 64
+  //         consecutive LDS words (no bank conflicts).  In load round t,
+  //         wavefront w takes rests (t*nwaves + w)*kRestsPerRound + i: every
+  //         rest field is wave-uniform (scalar registers) and kg is a
+  //         compile-time offset.
+  constexpr int kRestsPerRound = kAPT / 4;
   const int nwaves = nthreads >> 6;
   uint8_t* lds_a = smem;
   uint8_t* lds_sc = smem + g.lds_asc_off;
   const int rows_valid = min(MBW * 16, g.M - m0);
-  const int n_items = MODE == 1 ? ((rows_valid + 15) >> 4) * kswg * 256 : 0;
-  // valid: the item has an LDS slot to fill (a row < M); inside: its group
-  // lies below K (else it is quantized as zeros).  Both are uniform over a
-  // quad (same row, same group).
-  struct Item {
-    int r, jl, kg, p;
-    bool valid, inside;
-  };
+  const int n_rests = MODE == 1 ? ((rows_valid + 15) >> 4) * kswg : 0;
   const int groups = g.K / kGroup;
-  auto item = [&](int it) {
-    Item x;
-    x.p = it & 3;
-    const int r16 = (it >> 2) & 15;
-    x.kg = (it >> 6) & 3;
-    const int rest = it >> 8;
-    const int rg = (int)(((unsigned long long)rest * g.kswg_inv) >> 32);
-    x.jl = rest - rg * kswg;
-    x.r = rg * 16 + r16;
-    x.valid = it < n_items && x.r < rows_valid;
-    x.inside = x.valid && (jw0 + x.jl) * 4 + x.kg < groups;
+  const int r16 = lane >> 2;
+  struct Rest {
+    int rg, jl;
+    bool live;    // rest < n_rests: its LDS slots exist
+    int kg_end;   // K-groups kg < kg_end lie below K (<= 0 when not live)
+    bool row_ok;  // per lane: the lane's row is below M
+  };
+  auto rest_info = [&](int rest) {
+    Rest x;
+    x.rg = MBW == 1 ? 0 : (int)(((unsigned long long)rest * g.kswg_inv) >> 32);
+    x.jl = rest - x.rg * kswg;
+    x.live = rest < n_rests;
+    x.kg_end = x.live ? groups - (jw0 + x.jl) * 4 : 0;
+    x.row_ok = r16 < rows_valid - x.rg * 16;
     return x;
   };
-  // unused items read the workgroup's first element (always in bounds)
-  auto load_item = [&](const Item& x) {
-    const int r = x.inside ? x.r : 0;
-    const size_t col = x.inside ? ((size_t)(jw0 + x.jl) * kStep + x.kg * 32 + x.p * 8)
-                                : (size_t)jw0 * kStep;
-    const uint4 v = *reinterpret_cast<const uint4*>(g.a + (size_t)(m0 + r) * g.lda + col);
-    return v;
+  const uint16_t* a_first = g.a + (size_t)m0 * g.lda + (size_t)jw0 * kStep;
+  const size_t a_lane = (size_t)r16 * g.lda + (lane & 3) * 8;
+  auto load_rest = [&](const Rest& x, uint4* v) {
+    const uint16_t* base = a_first + (size_t)x.rg * 16 * g.lda + (size_t)x.jl * kStep;
+    const size_t lane_off = x.row_ok ? a_lane : (size_t)(lane & 3) * 8;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const uint16_t* src = (kg < x.kg_end ? base + kg * kGroup : a_first) + lane_off;
+      v[kg] = *reinterpret_cast<const uint4*>(src);
+    }
   };
-  auto quantize_item = [&](const Item& x, uint4 v) {
+  auto quantize_rest = [&](int rest, const Rest& x, const uint4* v) {
+    if (!x.live || !x.row_ok) return;
     const int jj = jw0 + x.jl;
-    const uint32_t amax = quad_max(amax8_bits(v));
-    const uint32_t byte = scale_byte_from_amax(amax);
-    const uint32_t codes = encode8(v, byte);
-    const int rg = x.r >> 4;
-    const int ln = (x.r & 15) + 16 * x.kg;
-    *reinterpret_cast<uint32_t*>(lds_a + ((size_t)(rg * kswg + x.jl) * 64 + ln) * 16 + 4 * x.p) =
-        codes;
-    if (x.p == 0)
-      lds_sc[((size_t)(rg * ngw + (jj >> 2) - gw0) * 64 + ln) * 4 + (jj & 3)] = (uint8_t)byte;
+    uint8_t* codes_at = lds_a + (size_t)rest * kBlockBytes + 4 * lane;
+    uint8_t* scale_at = lds_sc + ((size_t)(x.rg * ngw + (jj >> 2) - gw0) * 64 + r16) * 4 + (jj & 3);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      // groups past K are quantized as zeros: zero magnitudes, zero codes
+      const bool in = kg < x.kg_end;
+      const uint32_t amax = quad_max(amax8_bits(v[kg], in ? 0x7FFF7FFFu : 0u));
+      const uint32_t byte = scale_byte_from_amax(amax);
+      const uint32_t codes = encode8(v[kg], byte);
+      *reinterpret_cast<uint32_t*>(codes_at + kg * 256) = in ? codes : 0u;
+      if ((lane & 3) == 0) scale_at[kg * 64] = (uint8_t)byte;
+    }
   };
   uint4 araw[kAPT];
   if constexpr (MODE == 1) {
 #pragma unroll
-    for (int u = 0; u < kAPT; ++u) araw[u] = load_item(item(tid + u * nthreads));
+    for (int i = 0; i < kRestsPerRound; ++i)
+      load_rest(rest_info(wave * kRestsPerRound + i), araw + 4 * i);
   } else {
     const PackedDims da = {g.MT, g.KS, g.KG};
     const int mbv = min(MBW, g.MT - mg * MBW);
@@ -192,21 +204,17 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   }
 
   if constexpr (MODE == 1) {
-    const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < kAPT; ++u) {
-      const Item x = item(tid + u * nthreads);
-      if (x.valid) quantize_item(x, x.inside ? araw[u] : zero);
+    for (int i = 0; i < kRestsPerRound; ++i) {
+      const int rest = wave * kRestsPerRound + i;
+      quantize_rest(rest, rest_info(rest), araw + 4 * i);
     }
-    // further rounds (plans whose A stage exceeds kAPT items per thread)
-    for (int base = kAPT * nthreads; base < n_items; base += kAPT * nthreads) {
+    // further rounds (plans whose A stage exceeds kAPT chunks per wavefront)
+    for (int r0 = (nwaves + wave) * kRestsPerRound; r0 < n_rests; r0 += nwaves * kRestsPerRound) {
 #pragma unroll
-      for (int u = 0; u < kAPT; ++u) araw[u] = load_item(item(base + tid + u * nthreads));
+      for (int i = 0; i < kRestsPerRound; ++i) load_rest(rest_info(r0 + i), araw + 4 * i);
 #pragma unroll
-      for (int u = 0; u < kAPT; ++u) {
-        const Item x = item(base + tid + u * nthreads);
-        if (x.valid) quantize_item(x, x.inside ? araw[u] : zero);
-      }
+      for (int i = 0; i < kRestsPerRound; ++i) quantize_rest(r0 + i, rest_info(r0 + i), araw + 4 * i);
     }
   } else {
     __builtin_amdgcn_s_waitcnt(0);  // the LDS-direct copies
@@ -214,7 +222,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   __syncthreads();
 
   // ---- 3. block-scaled FP4 products.  Rows >= M get scale byte 0 and are
-  //         never stored.
+  //         never stored.  The wavefront's A scale dwords are read from LDS
+  //         once; A codes are read kAhead steps ahead of their product.
+  constexpr int kAhead = MBW >= 4 ? 2 : 3;  // LDS reads in flight stay within the wait counter
   uint32_t rowmask[MBW];
 #pragma unroll
   for (int b = 0; b < MBW; ++b) rowmask[b] = (m0 + b * 16 + (lane & 15)) < g.M ? 0xFFu : 0u;
@@ -225,61 +235,55 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < NTW; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A operands of one step for all MBW blocks; the next step's are read
-  // from LDS while the current step's products issue.
-  uint4 av[MBW];
-  uint32_t asd[MBW];
-  auto read_a = [&](int j, uint4 (&v)[MBW], uint32_t (&sd)[MBW]) {
-    const int jj = j0 + j;
+  uint32_t as[MBW][NSD];
+#pragma unroll
+  for (int b = 0; b < MBW; ++b)
+#pragma unroll
+    for (int d = 0; d < NSD; ++d) {
+      const int rel = min((j0 >> 2) + d - gw0, ngw - 1);
+      as[b][d] = *reinterpret_cast<const uint32_t*>(lds_sc + ((size_t)(b * ngw + rel) * 64 + lane) * 4);
+    }
+  uint4 av[KSW][MBW];  // statically indexed: only kAhead + 2 steps are live at once
+  auto read_a = [&](int j) {
     const int jl = wave_k * KSW + j;
 #pragma unroll
-    for (int b = 0; b < MBW; ++b) {
-      v[b] = *reinterpret_cast<const uint4*>(lds_a + ((size_t)(b * kswg + jl) * 64 + lane) * 16);
-      sd[b] = *reinterpret_cast<const uint32_t*>(
-          lds_sc + ((size_t)(b * ngw + (jj >> 2) - gw0) * 64 + lane) * 4);
-    }
+    for (int b = 0; b < MBW; ++b)
+      av[j][b] = *reinterpret_cast<const uint4*>(lds_a + ((size_t)(b * kswg + jl) * 64 + lane) * 16);
   };
-  read_a(0, av, asd);
+#pragma unroll
+  for (int j = 0; j <= kAhead && j < KSW; ++j) read_a(j);
 
 #pragma unroll
   for (int j = 0; j < KSW; ++j) {
-    uint4 avn[MBW];
-    uint32_t asdn[MBW];
-    if (j + 1 < KSW) read_a(j + 1, avn, asdn);
-    // keep the next step's LDS reads ahead of this step's products
+    if (j + kAhead + 1 < KSW) read_a(j + kAhead + 1);
+    // keep the later steps' LDS reads ahead of this step's products
     __builtin_amdgcn_sched_barrier(0);
+    // Scale bytes of step j: dword d of as/bs holds steps 4*((j0 >> 2) + d)
+    // .. +3, one byte each.  Where that dword is not known at compile time
+    // it is chosen by selects (an indexed access would move the arrays to
+    // scratch memory).
     const int jj = j0 + j;
     const int sh = (KSW % 4 == 0) ? 8 * (j & 3) : 8 * (jj & 3);
+    constexpr bool kStatic = KSW % 4 == 0 || KSW <= 2;
+    const int dsel = kStatic ? ((KSW % 4 == 0) ? (j >> 2) : 0) : (jj >> 2) - (j0 >> 2);
     int bsc[NTW];
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-      uint32_t w;
-      if constexpr (KSW % 4 == 0 || KSW <= 2) {
-        w = bs[i][(KSW % 4 == 0) ? (j >> 2) : 0];
-      } else {
-        // runtime choice among NSD registers by selects (no indexed access,
-        // which would move the array to scratch memory)
-        const int dsel = (jj >> 2) - (j0 >> 2);
-        w = bs[i][0];
+      uint32_t w = bs[i][0];
 #pragma unroll
-        for (int d = 1; d < NSD; ++d) w = (dsel == d) ? bs[i][d] : w;
-      }
+      for (int d = 1; d < NSD; ++d) w = (dsel == d) ? bs[i][d] : w;
       bsc[i] = (int)((w >> sh) & 0xFFu);
     }
 #pragma unroll
     for (int b = 0; b < MBW; ++b) {
-      const int asc = (int)((asd[b] >> sh) & rowmask[b]);
+      uint32_t w = as[b][0];
 #pragma unroll
-      for (int i = 0; i < NTW; ++i) acc[b][i] = mfma_fp4(av[b], bq[i][j], acc[b][i], asc, bsc[i]);
+      for (int d = 1; d < NSD; ++d) w = (dsel == d) ? as[b][d] : w;
+      const int asc = (int)((w >> sh) & rowmask[b]);
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) acc[b][i] = mfma_fp4(av[j][b], bq[i][j], acc[b][i], asc, bsc[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 < KSW) {
-#pragma unroll
-      for (int b = 0; b < MBW; ++b) {
-        av[b] = avn[b];
-        asd[b] = asdn[b];
-      }
-    }
   }
 
   // ---- 4. sum the wk wavefronts of one column group in LDS, in order.

@@ -56,11 +56,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Largest |bf16| of the 8 values in v, as a bf16 magnitude bit pattern.
 // Magnitude bit patterns of finite values order like the values themselves,
 // so packed 16-bit integer maxima do the work two values at a time.
-__device__ inline uint32_t amax8_bits(uint4 v) {
-  const u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
-  const u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
-  const u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
-  const u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+// mag_mask = 0 treats the 8 values as zeros.
+__device__ inline uint32_t amax8_bits(uint4 v, uint32_t mag_mask = 0x7FFF7FFFu) {
+  const u16x2 a = __builtin_bit_cast(u16x2, v.x & mag_mask);
+  const u16x2 b = __builtin_bit_cast(u16x2, v.y & mag_mask);
+  const u16x2 c = __builtin_bit_cast(u16x2, v.z & mag_mask);
+  const u16x2 d = __builtin_bit_cast(u16x2, v.w & mag_mask);
   const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
                                             __builtin_elementwise_max(c, d));
   return max((uint32_t)m.x, (uint32_t)m.y);
@@ -80,8 +81,9 @@ __device__ inline uint32_t quad_max(uint32_t x) {
 // significand is at least 1.75), take the biased exponent e; the unbiased
 // scale exponent is e - 127 - 2, clamped to [-127, 127]; the byte is that
 // plus 127, i.e. max(e - 2, 0).  (Rule of submission 752099 `_bf16_to_fp4_hw`.)
+// On the bf16 pattern the same steps read: add 2^5, exponent = bits 7..14.
 __device__ inline uint32_t scale_byte_from_amax(uint32_t amax_bf16_bits) {
-  uint32_t e = (((amax_bf16_bits << 16) + 0x00200000u) >> 23) & 0xFFu;
+  uint32_t e = ((amax_bf16_bits + 0x20u) >> 7) & 0xFFu;
   return e > 2u ? e - 2u : 0u;
 }
 
@@ -98,7 +100,9 @@ __device__ inline uint32_t scale_byte_from_amax(uint32_t amax_bf16_bits) {
 // tests repeat that sweep through the library against the CPU oracle.
 __device__ inline uint32_t encode8(uint4 v, uint32_t byte) {
   const float scale = __uint_as_float(byte << 23);
-  uint32_t r = 0;
+  // each convert writes one byte of r (selector 0..3), so all four bytes are
+  // written and the starting value (here v.x's register) never shows
+  uint32_t r = v.x;
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, v.x), scale, 0);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, v.y), scale, 1);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, v.z), scale, 2);

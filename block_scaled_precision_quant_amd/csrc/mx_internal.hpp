@@ -22,7 +22,7 @@ struct Plan {
 };
 
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kAPT = 8;              // fused A items (16 bytes) per thread per load round
+constexpr int kAPT = 8;              // fused A chunks per wavefront per load round (16 B per lane each)
 constexpr int kMaxLastWgSplit = 16;  // split_k bound for the last-workgroup reduce
 constexpr int kMaxThreads = 512;
 
