@@ -102,8 +102,14 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   const mx::GemmGeom g = mx::gemm_geometry(q, M, N, K);
   if (g.lds_total > (size_t)mx::kMaxLds)
     return fail(MXFP4_EINVAL, "plan needs %zu bytes of LDS (max %d)", g.lds_total, mx::kMaxLds);
-  if (8LL * ((long long)g.ngroups * p.split_k + 7) / 8 * g.mgroups > 0x7FFFFFFFLL)
-    return fail(MXFP4_EINVAL, "grid too large");
+  // a dispatch holds at most 2^32 - 1 work-items
+  const long long blocks = 8LL * (((long long)g.ngroups * p.split_k + 7) / 8) * g.mgroups;
+  if (blocks * g.threads > 0xFFFFFFFFLL)
+    return fail(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", blocks, g.threads);
+  if (p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_KERNEL) {
+    const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
+    if (n > 0xFFFFFFFFLL - 63) return fail(MXFP4_EINVAL, "split-K reduce grid too large (%lld threads)", n);
+  }
   return MXFP4_OK;
 }
 
@@ -140,9 +146,9 @@ mxfp4_plan default_plan(int M, int N, int K) {
       {4, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
       {32, 4096, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
       {32, 2880, 512, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 1, 4, 1)},
-      {16, 2112, 7168, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 2, 7, 4, MXFP4_REDUCE_KERNEL)},
+      {16, 2112, 7168, make_plan(MXFP4_MODE_FUSED, 1, 1, 4, 2, 4, 7, MXFP4_REDUCE_KERNEL)},
       {64, 7168, 2048, make_plan(MXFP4_MODE_FUSED, 1, 1, 8, 1, 16, 1)},
-      {256, 3072, 1536, make_plan(MXFP4_MODE_FUSED, 1, 2, 8, 1, 12, 1)},
+      {256, 3072, 1536, make_plan(MXFP4_MODE_FUSED, 2, 1, 8, 1, 12, 1)},
   };
   for (const Row& r : table)
     if (r.M == M && r.N == N && r.K == K) return r.p;

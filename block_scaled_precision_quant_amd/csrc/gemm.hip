@@ -400,19 +400,37 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 
 // Sum split fp32 partials [S][M][N] in order s = 0..S-1 and round to bf16.
 // With N % 4 == 0 one thread takes 4 consecutive outputs (16-byte loads);
-// otherwise one output.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
-                                                            uint16_t* __restrict__ c, int M,
-                                                            int N, int ldc, int S) {
+// otherwise one output.  The partials are loaded kRedChunk at a time, all of
+// a chunk requested before the first is added; one wavefront per workgroup
+// spreads the small grid over many CUs.
+constexpr int kRedChunk = 8;
+constexpr int kRedThreads = 64;
+
+template <typename V, typename Add>
+__device__ inline V sum_partials(const V* src, size_t plane, int S, Add add) {
+  V acc{};
+  for (int k0 = 0; k0 < S; k0 += kRedChunk) {
+    V v[kRedChunk];
+#pragma unroll
+    for (int u = 0; u < kRedChunk; ++u)
+      if (k0 + u < S) v[u] = src[(size_t)(k0 + u) * plane];
+#pragma unroll
+    for (int u = 0; u < kRedChunk; ++u)
+      if (k0 + u < S) acc = (k0 + u == 0) ? v[u] : add(acc, v[u]);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(kRedThreads) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                                    uint16_t* __restrict__ c,
+                                                                    int M, int N, int ldc, int S) {
   const size_t plane = (size_t)M * N;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if ((N & 3) != 0) {
     if (idx >= (long long)plane) return;
     const int row = (int)(idx / N);
     const int col = (int)(idx % N);
-    const float* src = ws + idx;
-    float acc = src[0];
-    for (int k = 1; k < S; ++k) acc += src[(size_t)k * plane];
+    const float acc = sum_partials(ws + idx, plane, S, [](float a, float b) { return a + b; });
     c[(size_t)row * ldc + col] = f32_to_bf16_rne(acc);
     return;
   }
@@ -420,15 +438,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (idx >= (long long)M * n4) return;
   const int row = (int)(idx / n4);
   const int col = (int)(idx % n4) * 4;
-  const float* src = ws + (size_t)row * N + col;
-  float4 acc = *reinterpret_cast<const float4*>(src);
-  for (int k = 1; k < S; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * plane);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
+  const float4 acc = sum_partials(reinterpret_cast<const float4*>(ws + (size_t)row * N + col),
+                                  plane / 4, S, [](float4 a, float4 b) {
+                                    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+                                  });
   uint16_t* dst = c + (size_t)row * ldc + col;
   const uint16_t h0 = f32_to_bf16_rne(acc.x), h1 = f32_to_bf16_rne(acc.y);
   const uint16_t h2 = f32_to_bf16_rne(acc.z), h3 = f32_to_bf16_rne(acc.w);
@@ -562,9 +575,9 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   if (e != hipSuccess) return e;
   if (p.split > 1 && !p.last_wg) {
     const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, M, N, ldc,
-                       p.split);
+    const unsigned grid = (unsigned)((n + kRedThreads - 1) / kRedThreads);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, ws, c, M, N,
+                       ldc, p.split);
     e = hipGetLastError();
   }
   return e;

@@ -102,6 +102,15 @@ def test_plan_checks(lib):
     assert check(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 8, 16, 1), k=16384) == EINVAL
     assert "LDS" in mx.load().mxfp4_last_error().decode()
     assert check(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 1, 16, 1)) == 0
+    # a dispatch holds at most 2^32 - 1 work-items: 2^32 workgroups of 64 threads
+    assert check(mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 1, 1), m=1 << 20, n=1 << 20, k=128) == EINVAL
+    assert "grid too large" in mx.load().mxfp4_last_error().decode()
+    # 2^17 x 2^17 with a 2-way split: the GEMM grid fits, the reduce kernel's 2^32 threads do not
+    big = mx.Plan(mx.MODE_FUSED, 4, 2, 8, 1, 1, 2, mx.REDUCE_KERNEL)
+    assert check(big, m=1 << 17, n=1 << 17, k=256) == EINVAL
+    assert "reduce grid" in mx.load().mxfp4_last_error().decode()
+    assert check(mx.Plan(*(list(big.__dict__.values())[:7] + [mx.REDUCE_LAST_WG])),
+                 m=1 << 17, n=1 << 17, k=256) == 0
 
 
 @no_gpu

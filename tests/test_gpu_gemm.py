@@ -202,6 +202,36 @@ def test_split_reduce_modes_agree(name, plan):
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("name,plan", [
+    ("m16_n2112_k7168", mx.Plan(F, 1, 1, 4, 2, 4, 7, mx.REDUCE_LAST_WG)),
+    ("m16_n2112_k7168", mx.Plan(F, 1, 1, 4, 2, 4, 7, mx.REDUCE_KERNEL)),
+    ("m64_n7168_k2048", mx.Plan(F, 4, 1, 2, 1, 4, 4, mx.REDUCE_LAST_WG)),
+    ("m4_n2880_k512", mx.Plan(F, 1, 2, 1, 1, 1, 4, mx.REDUCE_LAST_WG)),
+])
+def test_split_no_stale_partials(name, plan):
+    """Back-to-back calls on one workspace with A, then -A: the second call
+    must give exactly -C (quantization is sign-symmetric and the K order is
+    fixed), so partials left by the first call can never be read back."""
+    w = inputs.WORKLOADS[name]
+    print("case", name, plan, flush=True)
+    ref = reference(name)
+    a = to_dev_bf16(ref["a_bits"])
+    neg = to_dev_bf16(ref["a_bits"] ^ np.uint16(0x8000))
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    ws = workspace(w.M, w.N, w.K, plan, a.device)
+    outs = []
+    for x in (a, neg, a, neg):
+        c = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device=a.device)
+        mx.gemm(x, b_packed, w.N, out=c, workspace=ws, plan=plan)
+        outs.append(c)  # no synchronization between the calls
+    torch.cuda.synchronize()
+    outs = [bf16_out_to_f32(c) for c in outs]
+    assert_close_to_oracle(outs[0], ref["c32"], "%s %s" % (name, plan))
+    for i in range(1, 4):
+        want = outs[0] if i % 2 == 0 else -outs[0]
+        assert np.array_equal(outs[i], want), (name, plan, i)
+
+
 def test_bitwise_repeatable():
     ref = reference("m16_n2112_k7168")
     p = mx.default_plan(16, 2112, 7168)
