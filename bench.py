@@ -107,6 +107,12 @@ def time_cold(torch, flush, fn, steps, warmup):
     return us
 
 
+def trimmed_mean(us):
+    """Mean without the single lowest and highest sample."""
+    s = sorted(us)
+    return statistics.fmean(s[1:-1]) if len(s) > 2 else statistics.fmean(s)
+
+
 def kernel_sources_sha():
     """sha256 over the HIP sources; hardware byte counters recorded under
     profiles/ are only reported while the kernels are unchanged."""
@@ -134,30 +140,54 @@ def recorded_traffic(workload):
 
 
 def cpu_baseline(names, seconds):
-    """The oracle as it stands (single thread), on the same inputs: quantize A,
-    dequantize A and B, fp32 dot.  B's quantization is excluded, as it is in
-    the GPU call (B arrives pre-quantized)."""
+    """The oracle as it stands, on the same inputs: quantize A, dequantize A
+    and B, fp32 dot.  B's quantization is excluded, as it is in the GPU call
+    (B arrives pre-quantized).  Timed on one thread, then on every host core
+    the process may use (at most 16): one thread per core, each running
+    whole oracle calls (the oracle's C routines release the interpreter
+    lock).  About 2*seconds of CPU work in all."""
+    import threading
+
     import oracle
     prepared = []
     for n in names:
         a, b = inputs.make(n)
         bq, bs = oracle.quantize(b)
         prepared.append((a, bq, bs))
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        for a, bq, bs in prepared:
-            aq, asc = oracle.quantize(a)
-            ad = oracle.dequantize(aq, asc)
-            bd = oracle.dequantize(bq, bs)
-            oracle.gemm(ad, bd, want64=False)
-            calls += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": dt / calls * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": "%d full oracle calls over the workload's shapes (%s), %.1f s, 1 thread"
-                      % (calls, ", ".join(names), dt)}
+
+    def one_call(a, bq, bs):
+        aq, asc = oracle.quantize(a)
+        ad = oracle.dequantize(aq, asc)
+        bd = oracle.dequantize(bq, bs)
+        oracle.gemm(ad, bd, want64=False)
+
+    def run(threads, wall_s):
+        counts = [0] * threads
+        stop = time.perf_counter() + wall_s
+
+        def worker(i):
+            while True:
+                for x in prepared:
+                    one_call(*x)
+                    counts[i] += 1
+                if time.perf_counter() >= stop:
+                    return
+        t0 = time.perf_counter()
+        ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        return time.perf_counter() - t0, sum(counts)
+
+    dt1, n1 = run(1, seconds / 2)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    dtn, nn = run(cores, max(1.0, seconds * 1.5 / cores))
+    return {"value": dtn / nn * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
+            "single_thread_value": dt1 / n1 * 1e6,
+            "sample": "full oracle calls over the workload's shapes (%s): %d calls on %d threads "
+                      "in %.1f s wall; single thread: %d calls in %.1f s"
+                      % (", ".join(names), nn, cores, dtn, n1, dt1)}
 
 
 def main():
@@ -203,7 +233,8 @@ def main():
     for c in cases:
         us = [a.elapsed_time(b) * 1000.0 for a, b in ev[c.name]]
         per[c.name] = {"median_us": statistics.median(us), "mean_us": statistics.fmean(us),
-                       "min_us": min(us), "plan": c.plan.__dict__,
+                       "trimmed_mean_us": trimmed_mean(us), "min_us": min(us),
+                       "plan": c.plan.__dict__,
                        "alg_bytes": alg_bytes(c.M, c.N, c.K), "flops": 2 * c.M * c.N * c.K}
     value = statistics.fmean(p["median_us"] for p in per.values())
 
@@ -263,6 +294,7 @@ def main():
             b = alg_bytes(c.M, c.N, c.K)
             print(json.dumps({"shape": n, "plan": c.plan.__dict__, "median_us": round(med, 3),
                               "mean_us": round(statistics.fmean(us), 3),
+                              "trimmed_mean_us": round(trimmed_mean(us), 3),
                               "hbm_GBps": round(b / (med * 1e-6) / 1e9, 1),
                               "mfma_frac_fp4": round(2 * c.M * c.N * c.K / (med * 1e-6) / 1e12
                                                      / FP4_PEAK_TFLOPS, 5),
