@@ -15,7 +15,8 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "REDUCE_KERNEL", "REDUCE_LAST_WG", "library_path", "load", "packed_bytes",
+    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "REDUCE_KERNEL", "REDUCE_LAST_WG",
+    "REDUCE_ATOMIC", "library_path", "load", "packed_bytes",
     "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes", "gemm",
     "gemm_prequant", "version",
 ]
@@ -25,6 +26,7 @@ MODE_FUSED = 1
 MODE_PREQUANT = 2
 REDUCE_KERNEL = 0
 REDUCE_LAST_WG = 1
+REDUCE_ATOMIC = 2
 
 _ERR_NAMES = {-1: "EINVAL", -2: "ENULL", -3: "EWORKSPACE", -4: "ESIZE", -5: "ENOTSUP", -6: "EHIP"}
 

@@ -44,7 +44,7 @@ mx::Plan to_internal(const mxfp4_plan& p) {
   q.wk = p.waves_k;
   q.ksw = p.k_steps_per_wave;
   q.split = p.split_k;
-  q.last_wg = p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_LAST_WG;
+  q.reduce = p.split_k > 1 ? p.split_reduce : mx::kReduceKernel;
   return q;
 }
 
@@ -79,8 +79,10 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
       p.k_steps_per_wave < 1 || p.split_k < 1)
     return fail(MXFP4_EINVAL, "plan fields must all be >= 1");
-  if (p.split_reduce != MXFP4_REDUCE_KERNEL && p.split_reduce != MXFP4_REDUCE_LAST_WG)
-    return fail(MXFP4_EINVAL, "plan.split_reduce must be MXFP4_REDUCE_KERNEL or MXFP4_REDUCE_LAST_WG (got %d)",
+  if (p.split_reduce != MXFP4_REDUCE_KERNEL && p.split_reduce != MXFP4_REDUCE_LAST_WG &&
+      p.split_reduce != MXFP4_REDUCE_ATOMIC)
+    return fail(MXFP4_EINVAL,
+                "plan.split_reduce must be MXFP4_REDUCE_KERNEL, _LAST_WG or _ATOMIC (got %d)",
                 p.split_reduce);
   if (p.split_k > mx::kMaxLastWgSplit && p.split_reduce == MXFP4_REDUCE_LAST_WG)
     return fail(MXFP4_EINVAL, "split_reduce LAST_WG supports split_k <= %d (got %d)", mx::kMaxLastWgSplit,
@@ -113,24 +115,32 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
   return MXFP4_OK;
 }
 
-// Workspace layout: [tile counters][MX-packed A][fp32 partials], each part
-// rounded up to 256 bytes.
+// Workspace layout: [tile counters][fp32 partials or accumulator][MX-packed A],
+// each part rounded up to 256 bytes.  The counters, and the accumulator of
+// the atomic reduce, must start at zero and are left zero by every call.
 struct WsLayout {
-  size_t counters, a, partials;  // byte sizes
-  size_t a_off() const { return counters; }
-  size_t part_off() const { return counters + a; }
-  size_t total() const { return counters + a + partials; }
+  size_t counters, partials, a;  // byte sizes
+  bool zero_partials;            // the partials part is the atomic accumulator
+  size_t part_off() const { return counters; }
+  size_t a_off() const { return counters + partials; }
+  size_t zero_bytes() const { return counters + (zero_partials ? partials : 0); }
+  size_t total() const { return counters + partials + a; }
 };
 
 WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
-  WsLayout w = {0, 0, 0};
-  if (p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_LAST_WG) {
+  WsLayout w = {0, 0, 0, false};
+  const bool split = p.split_k > 1;
+  if (split && p.split_reduce != MXFP4_REDUCE_KERNEL) {
     const mx::GemmGeom g = mx::gemm_geometry(to_internal(p), M, N, K);
     w.counters = round_up((size_t)g.mgroups * g.ngroups * 4, 256);
   }
+  if (split) {
+    const size_t planes = p.split_reduce == MXFP4_REDUCE_ATOMIC ? 1 : (size_t)p.split_k;
+    w.partials = round_up(planes * M * N * 4, 256);
+    w.zero_partials = p.split_reduce == MXFP4_REDUCE_ATOMIC;
+  }
   if (!prequant_entry && p.mode == MXFP4_MODE_PREQUANT)
     w.a = round_up(mxfp4_packed_bytes(M, K), 256);
-  if (p.split_k > 1) w.partials = round_up((size_t)p.split_k * M * N * 4, 256);
   return w;
 }
 
@@ -297,7 +307,7 @@ size_t mxfp4_plan_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
 size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan* plan, int M, int N, int K) {
   if (!plan || check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
   if (check_plan(*plan, M, N, K, false) != MXFP4_OK) return 0;
-  return ws_layout(*plan, M, N, K, false).counters;
+  return ws_layout(*plan, M, N, K, false).zero_bytes();
 }
 
 size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {

@@ -26,12 +26,12 @@ struct GemmArgs {
   const uint8_t* ap;  // MX-packed A (prequant mode)
   const uint8_t* bp;  // MX-packed B
   uint16_t* c;        // bf16 C [M][ldc]
-  float* ws;          // fp32 partials [split][M][N]
+  float* ws;          // fp32 partials [split][M][N], or the [M][N] accumulator (atomic reduce)
   unsigned* counters; // per output tile arrival counters (last-workgroup reduce)
   int M, N, K, lda, ldc;
   int MT, NT, KS, KG;
   int wn, wk, split, mgroups, ngroups, kswg;
-  int last_wg_reduce;  // split > 1: 1 = last workgroup sums, 0 = reduce kernel
+  int reduce;          // split > 1: a Reduce value
   unsigned lds_asc_off, lds_red_off;
   unsigned long long kswg_inv;  // floor(2^32 / kswg) + 1: x / kswg == (x * kswg_inv) >> 32
                                 // for every x < 2^32 / kswg (33-bit for kswg = 1)
@@ -330,7 +330,10 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
           float* part = g.ws + ((size_t)s * g.M + row) * g.N + col;
           if (g.split == 1)
             g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[b][i][e]);
-          else if (g.last_wg_reduce)
+          else if (g.reduce == kReduceAtomic)
+            __hip_atomic_fetch_add(g.ws + (size_t)row * g.N + col, acc[b][i][e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          else if (g.reduce == kReduceLastWg)
             __hip_atomic_store(part, acc[b][i][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           else
             *part = acc[b][i][e];
@@ -338,18 +341,22 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
       }
     }
   }
-  if (g.split == 1 || !g.last_wg_reduce) return;
+  if (g.split == 1 || g.reduce == kReduceKernel) return;
 
   // ---- 6. split-K finished by the last workgroup of this output tile.
-  //         The partials above are agent-scope atomic stores, which are
-  //         coherent across the XCDs' L2 caches without an L2 write-back;
-  //         once they have completed (waitcnt) the tile counter is bumped,
-  //         and the workgroup that takes it to split-1 reads the partials
-  //         with agent-scope atomic loads, sums them in order
-  //         s = 0..split-1 (the order of splitk_reduce_kernel, so both
-  //         reductions give identical bits) and returns the counter to zero
-  //         for the next call on this workspace.  The flag lives in the first
-  //         LDS word: every LDS read above is behind the first barrier here.
+  //         The partials above are agent-scope atomic stores (or, for the
+  //         atomic reduce, agent-scope atomic adds into one accumulator),
+  //         which are coherent across the XCDs' L2 caches without an L2
+  //         write-back; once they have completed (waitcnt) the tile counter
+  //         is bumped, and the workgroup that takes it to split-1 reads them
+  //         with agent-scope atomic loads.  Last-workgroup reduce: the
+  //         partials are summed in order s = 0..split-1 (the order of
+  //         splitk_reduce_kernel, so both give identical bits).  Atomic
+  //         reduce: the accumulator already holds the sum (its order of
+  //         additions varies from call to call) and is cleared again.  The
+  //         counter returns to zero for the next call on this workspace.  The
+  //         flag lives in the first LDS word: every LDS read above is behind
+  //         the first barrier here.
   volatile int* is_last = reinterpret_cast<volatile int*>(smem);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -361,7 +368,34 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   }
   __syncthreads();
   if (!*is_last) return;
-  if (owner) {
+  if (owner && g.reduce == kReduceAtomic) {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = nt_base + i;
+      if (nt >= g.NT) continue;
+      const int col = nt * 16 + (lane & 15);
+#pragma unroll
+      for (int b = 0; b < MBW; ++b) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
+          if (row < g.M && col < g.N)
+            v[e] = __hip_atomic_load(g.ws + (size_t)row * g.N + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + b * 16 + 4 * (lane >> 4) + e;
+          if (row < g.M && col < g.N) {
+            g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(v[e]);
+            __hip_atomic_store(g.ws + (size_t)row * g.N + col, 0.0f, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+  } else if (owner) {
     const size_t plane = (size_t)g.M * g.N;
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
@@ -550,7 +584,7 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   args.c = c;
   args.ws = ws;
   args.counters = counters;
-  args.last_wg_reduce = p.last_wg ? 1 : 0;
+  args.reduce = p.split > 1 ? p.reduce : kReduceKernel;
   args.M = M;
   args.N = N;
   args.K = K;
@@ -573,7 +607,7 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   hipError_t e = hipLaunchKernel(fn, dim3(geo.grid), dim3(geo.threads), kargs,
                                  (unsigned)geo.lds_total, stream);
   if (e != hipSuccess) return e;
-  if (p.split > 1 && !p.last_wg) {
+  if (p.split > 1 && p.reduce == kReduceKernel) {
     const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
     const unsigned grid = (unsigned)((n + kRedThreads - 1) / kRedThreads);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, ws, c, M, N,

@@ -18,7 +18,15 @@ struct Plan {
   int wk;        // wavefronts along K
   int ksw;       // 128-K steps per wavefront
   int split;     // workgroups along K
-  int last_wg;   // split > 1: the last workgroup of a tile sums the partials
+  int reduce;    // split > 1: how the K slices are summed (Reduce)
+};
+
+// Split-K reductions (values match MXFP4_REDUCE_* in mxfp4.h).
+enum Reduce : int {
+  kReduceKernel = 0,  // fp32 partials [split][M][N], splitk_reduce_kernel
+  kReduceLastWg = 1,  // fp32 partials; the last workgroup of each tile sums them
+  kReduceAtomic = 2,  // fp32 atomic adds into one [M][N] accumulator; the last
+                      // workgroup of each tile converts it and clears it
 };
 
 constexpr int kMaxLds = 160 * 1024;
@@ -46,9 +54,11 @@ GemmGeom gemm_geometry(const Plan& p, int M, int N, int K);
 bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw);
 
 // Enqueue the GEMM kernel (and the split-K reduce kernel when p.split > 1
-// and !p.last_wg).
-//   a: bf16 A (fused) or MX-packed A (prequant); ws: fp32 partials;
-//   counters: mgroups*ngroups zeroed tile counters (p.last_wg only).
+// and p.reduce == kReduceKernel).
+//   a: bf16 A (fused) or MX-packed A (prequant); ws: fp32 partials
+//   [split][M][N], or the zeroed [M][N] accumulator for kReduceAtomic;
+//   counters: mgroups*ngroups zeroed tile counters (kReduceLastWg and
+//   kReduceAtomic).
 hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_packed,
                        uint16_t* c, int ldc, int M, int N, int K, float* ws,
                        unsigned* counters, hipStream_t stream);

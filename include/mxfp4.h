@@ -118,7 +118,12 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * reduce kernel (split_reduce = MXFP4_REDUCE_KERNEL) or, in the same launch,
  * in the last workgroup to finish each output tile, found with a per-tile
  * arrival counter in the workspace (MXFP4_REDUCE_LAST_WG).  Both give the
- * same bits.
+ * same bits.  MXFP4_REDUCE_ATOMIC instead adds every slice's fp32 partial
+ * into one [M][N] accumulator in the workspace with atomic adds, and the last
+ * workgroup of each tile rounds the sum to bf16 and clears the accumulator;
+ * the order of the additions varies from call to call, so its results agree
+ * with the others within the fp32 rounding of a different summation order,
+ * not bit for bit.
  *
  * mode FUSED quantizes the workgroup's A rows inside the GEMM kernel; mode
  * PREQUANT first runs the quantizer once into the workspace (MX-packed) and
@@ -129,6 +134,7 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
 
 #define MXFP4_REDUCE_KERNEL 0
 #define MXFP4_REDUCE_LAST_WG 1
+#define MXFP4_REDUCE_ATOMIC 2
 
 typedef struct mxfp4_plan {
     int mode;             /* MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT */
@@ -138,8 +144,8 @@ typedef struct mxfp4_plan {
     int waves_k;          /* wavefronts along K per workgroup (in-LDS reduce) */
     int k_steps_per_wave; /* 128-K steps per wavefront: 1,2,3,4,6,7,8,12,14,16 */
     int split_k;          /* workgroups along K (fp32 workspace + reduce) */
-    int split_reduce;     /* split_k > 1: MXFP4_REDUCE_KERNEL or MXFP4_REDUCE_LAST_WG
-                             (LAST_WG needs split_k <= 16) */
+    int split_reduce;     /* split_k > 1: MXFP4_REDUCE_KERNEL, MXFP4_REDUCE_LAST_WG
+                             (needs split_k <= 16) or MXFP4_REDUCE_ATOMIC */
 } mxfp4_plan;
 
 /* The plan mxfp4_gemm uses for a shape (a per-shape table for the tuned
@@ -152,18 +158,20 @@ int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
 int mxfp4_check_plan(const mxfp4_plan *plan, int M, int N, int K);
 
 /* Workspace bytes a plan needs for a shape, laid out as
- *   [tile counters][MX-packed A][fp32 partials]
+ *   [tile counters][fp32 partials or accumulator][MX-packed A]
  * with each part rounded up to 256 bytes: tile counters (4 bytes per
- * workgroup tile) when split_k > 1 and split_reduce is LAST_WG; the MX-packed
- * A in PREQUANT mode; split_k*M*N*4 bytes of partials when split_k > 1.
+ * workgroup tile) when split_k > 1 and split_reduce is LAST_WG or ATOMIC;
+ * split_k*M*N*4 bytes of partials when split_k > 1 (M*N*4 bytes, one
+ * accumulator, for ATOMIC); the MX-packed A in PREQUANT mode.
  * 0 when none is needed or the plan is invalid. */
 size_t mxfp4_plan_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
 
-/* Leading workspace bytes (the tile counters) that must be zero before the
- * first call that uses the workspace with this plan; every completed call
- * leaves them zero again, so one zero-fill per workspace suffices.  Calls
- * that share one workspace must not overlap in time.  The rest of the
- * workspace is scratch.  0 when the plan keeps no counters. */
+/* Leading workspace bytes (the tile counters, and for ATOMIC the
+ * accumulator after them) that must be zero before the first call that uses
+ * the workspace with this plan; every completed call leaves them zero again,
+ * so one zero-fill per workspace suffices.  Calls that share one workspace
+ * must not overlap in time.  The rest of the workspace is scratch.  0 when
+ * the plan keeps no counters. */
 size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan *plan, int M, int N, int K);
 
 /* Workspace bytes of the default plan (same layout and zero-fill rule). */
@@ -189,16 +197,16 @@ int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_pac
                   uint16_t *c, int ldc, int M, int N, int K, void *workspace,
                   size_t workspace_bytes, const mxfp4_plan *plan, void *stream);
 
+/* Workspace bytes of mxfp4_gemm_prequant for a plan (NULL = default plan);
+ * its zero-fill prefix is mxfp4_plan_workspace_zero_bytes of the same plan. */
+size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
+
 /* GEMM on an A that is already MX-packed (from mxfp4_quant_a_packed), for
  * callers that quantize one activation once and use it against several
  * weights.  The plan's mode is ignored (the kernel reads fp4 A); NULL plan =
  * the default plan's tiling.  Workspace: as for mxfp4_gemm_ex with the plan in
  * PREQUANT mode, minus the MX-packed A part (tile counters, then partials).
  * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
-/* Workspace bytes of mxfp4_gemm_prequant for a plan (NULL = default plan);
- * its zero-fill prefix is mxfp4_plan_workspace_zero_bytes of the same plan. */
-size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
-
 int mxfp4_gemm_prequant(const void *a_packed, size_t a_packed_bytes, const void *b_packed,
                         size_t b_packed_bytes, uint16_t *c, int ldc, int M, int N, int K,
                         void *workspace, size_t workspace_bytes, const mxfp4_plan *plan,

@@ -97,6 +97,8 @@ def test_plan_checks(lib):
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 1)) == 0         # last-WG reduce: split <= 16
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, 1), k=4096) == EINVAL
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, 0), k=4096) == 0
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, mx.REDUCE_ATOMIC), k=4096) == 0  # any split
+    assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 3)) == EINVAL                    # split_reduce
     assert check(mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, 7)) == EINVAL  # split_reduce
     # 64 rows x 128 K-steps of packed A per workgroup do not fit in LDS
     assert check(mx.Plan(mx.MODE_FUSED, 4, 1, 1, 8, 16, 1), k=16384) == EINVAL
@@ -147,6 +149,17 @@ def test_workspace_sizes(lib):
     assert mx.workspace_bytes(M, N, K, pq) == 256 + (mx.packed_bytes(M, K) + 255) // 256 * 256 \
         + 4 * M * N * 4
     assert mx.prequant_workspace_bytes(M, N, K, pq) == 256 + 4 * M * N * 4
+    # atomic reduce: one zeroed [M][N] fp32 accumulator after the counters
+    at = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_ATOMIC)
+    assert mx.workspace_zero_bytes(M, N, K, at) == 256 + M * N * 4
+    assert mx.workspace_bytes(M, N, K, at) == 256 + M * N * 4
+    atq = mx.Plan(mx.MODE_PREQUANT, 1, 1, 1, 1, 4, 4, mx.REDUCE_ATOMIC)
+    assert mx.workspace_bytes(M, N, K, atq) == 256 + M * N * 4 + \
+        (mx.packed_bytes(M, K) + 255) // 256 * 256
+    assert mx.workspace_zero_bytes(M, N, K, atq) == 256 + M * N * 4
+    # without a split the reduce mode needs nothing
+    one = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 16, 1, mx.REDUCE_ATOMIC)
+    assert mx.workspace_bytes(M, N, K, one) == 0 == mx.workspace_zero_bytes(M, N, K, one)
 
 
 @no_gpu

@@ -232,6 +232,38 @@ def test_split_no_stale_partials(name, plan):
         assert np.array_equal(outs[i], want), (name, plan, i)
 
 
+@pytest.mark.parametrize("shape,plan", [
+    ("m16_n2112_k7168", mx.Plan(F, 1, 1, 4, 2, 4, 7, mx.REDUCE_ATOMIC)),
+    ("m16_n2112_k7168", mx.Plan(P, 1, 1, 1, 2, 7, 4, mx.REDUCE_ATOMIC)),
+    ("m64_n7168_k2048", mx.Plan(F, 4, 1, 2, 1, 4, 4, mx.REDUCE_ATOMIC)),
+    ("m4_n2880_k512", mx.Plan(F, 1, 2, 1, 1, 1, 4, mx.REDUCE_ATOMIC)),
+    ((33, 1000, 1504, 40), mx.Plan(F, 1, 2, 2, 1, 3, 4, mx.REDUCE_ATOMIC)),
+    ((17, 24, 4128, 41), mx.Plan(F, 2, 1, 1, 3, 1, 11, mx.REDUCE_ATOMIC)),
+])
+def test_split_atomic_reduce(shape, plan):
+    """fp32 atomic adds into one accumulator: within tolerance on every call,
+    the accumulator and counters back at zero after each call, and a call on
+    -A right after one on A gives -C within tolerance (its order of
+    additions differs, so not bit for bit)."""
+    print("case", shape, plan, flush=True)
+    ref = reference(shape)
+    M, K = ref["a_bits"].shape
+    N = ref["bq"].shape[0]
+    a = to_dev_bf16(ref["a_bits"])
+    neg = to_dev_bf16(ref["a_bits"] ^ np.uint16(0x8000))
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    ws = workspace(M, N, K, plan, a.device)
+    nz = mx.workspace_zero_bytes(M, N, K, plan)
+    assert nz > M * N * 4
+    for i, x in enumerate((a, neg, a)):
+        c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=a.device)
+        mx.gemm(x, b_packed, N, out=c, workspace=ws, plan=plan)
+        torch.cuda.synchronize()
+        want = ref["c32"] if i % 2 == 0 else -ref["c32"]
+        assert_close_to_oracle(bf16_out_to_f32(c), want, "%s %s call %d" % (shape, plan, i))
+        assert int(ws[:nz].count_nonzero()) == 0  # counters and accumulator cleared
+
+
 def test_bitwise_repeatable():
     ref = reference("m16_n2112_k7168")
     p = mx.default_plan(16, 2112, 7168)
