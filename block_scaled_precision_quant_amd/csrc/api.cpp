@@ -92,7 +92,7 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
     return fail(MXFP4_ENOTSUP,
                 "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this build",
                 p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
-  const int KS = (K + 127) / 128;
+  const int KS = (int)(((long long)K + 127) / 128);
   if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
     return fail(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal ceil(K/128))",
                 (long long)p.split_k * p.waves_k * p.k_steps_per_wave, KS);
@@ -169,8 +169,8 @@ mxfp4_plan default_plan(int M, int N, int K) {
   // per wavefront that divides the K steps (at most 16), then up to two
   // wavefronts along K inside the workgroup and the rest as workgroups along
   // K summed by the reduce kernel.
-  const int KS = (K + 127) / 128;
-  const int NT = (N + 15) / 16;
+  const int KS = (int)(((long long)K + 127) / 128);
+  const int NT = (int)(((long long)N + 15) / 16);
   static const int ksw_opts[] = {16, 14, 12, 8, 7, 6, 4, 3, 2, 1};
   int ksw = 1;
   for (int k : ksw_opts)
@@ -182,7 +182,7 @@ mxfp4_plan default_plan(int M, int N, int K) {
   int wn = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
   int wk = (rest % 2 == 0) ? 2 : 1;
   // a grid already wide without K splits keeps K inside the workgroup
-  const long long wide = (long long)((M + 15) / 16) * ((NT + wn - 1) / wn);
+  const long long wide = (((long long)M + 15) / 16) * ((NT + wn - 1) / wn);
   if (wide >= 512 && rest > 1) {
     wn = 2;
     wk = 1;

@@ -72,7 +72,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   // workgroup i runs on XCD i % 8.  The mgroups row groups of one column
   // task (same B tiles, same K range) get ids that are equal mod 8 and land
   // on one XCD, where the first read of each B tile fills the L2 for the
-  // rest.  Ids past the last task (padding of the final round) exit at once.
+  // rest.  The placement only affects speed: every workgroup computes the
+  // same thing wherever it runs.  Ids past the last task (padding of the
+  // final round) exit at once.
   const int tasks = g.ngroups * g.split;
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
@@ -546,13 +548,13 @@ bool gemm_kernel_available(int mode, int mbw, int ntw, int ksw) {
 GemmGeom gemm_geometry(const Plan& p, int M, int N, int K) {
   GemmGeom g;
   const PackedDims bd = packed_dims(N, K);
-  g.MT = (M + 15) / 16;
+  g.MT = (int)(((long long)M + 15) / 16);
   g.NT = bd.RT;
   g.KS = bd.KS;
   g.KG = bd.KG;
-  g.mgroups = (g.MT + p.mbw - 1) / p.mbw;
+  g.mgroups = (int)(((long long)g.MT + p.mbw - 1) / p.mbw);
   const int cols_per_wg = p.wn * p.ntw;
-  g.ngroups = (g.NT + cols_per_wg - 1) / cols_per_wg;
+  g.ngroups = (int)(((long long)g.NT + cols_per_wg - 1) / cols_per_wg);
   g.kswg = p.wk * p.ksw;
   g.ngw_max = (g.kswg % 4 == 0) ? g.kswg / 4 : (g.kswg + 6) / 4;
   g.lds_a = (size_t)p.mbw * g.kswg * kBlockBytes;

@@ -36,8 +36,8 @@ struct PackedDims {
 // scale 127 (a zero contribution).
 __host__ __device__ inline PackedDims packed_dims(int rows, int K) {
   PackedDims d;
-  d.RT = (rows + kTileRows - 1) / kTileRows;
-  d.KS = (K + kStep - 1) / kStep;
+  d.RT = (int)(((long long)rows + kTileRows - 1) / kTileRows);  // no overflow near INT_MAX
+  d.KS = (int)(((long long)K + kStep - 1) / kStep);
   d.KG = (d.KS + 3) / 4;
   return d;
 }
