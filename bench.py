@@ -125,8 +125,10 @@ def kernel_sources_sha():
     return h.hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch from the committed counter summary, or None."""
+def recorded_profile(workload):
+    """The committed rocprofv3 record for the workload (HBM bytes per launch
+    from the FETCH_SIZE/WRITE_SIZE runs, median traced kernel duration), or
+    None when the kernel sources have changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -136,7 +138,7 @@ def recorded_traffic(workload):
     entry = rec.get(workload)
     if not entry or entry.get("kernel_sources_sha") != kernel_sources_sha():
         return None
-    return entry.get("bytes_per_launch")
+    return entry
 
 
 def cpu_baseline(names, seconds):
@@ -251,6 +253,7 @@ def main():
     mean_us = statistics.fmean(p["mean_us"] for p in per.values())
     achieved = tot_bytes / len(per) / (mean_us * 1e-6) / 1e9
     tot_flops = sum(p["flops"] for p in per.values())
+    prof = recorded_profile(args.workload)
     for c in cases:
         p = per[c.name]
         p["hbm_GBps"] = p["alg_bytes"] / (p["median_us"] * 1e-6) / 1e9
@@ -275,9 +278,15 @@ def main():
             "M=%d N=%d K=%d" % (c.M, c.N, c.K) for c in cases), "shapes": per},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic(args.workload),
+                     "traffic": prof and prof.get("bytes_per_launch"),
                      "kernel": "gemm_kernel (one launch per call)",
-                     "launch_us_mean": round(mean_us, 3)},
+                     "launch_us_mean": round(mean_us, 3),
+                     # the same kernel's rocprofv3 duration (committed trace of this
+                     # command): the event pair also brackets dispatch overhead
+                     "kernel_us_rocprof": prof and prof.get("kernel_ns_median") and
+                     round(prof["kernel_ns_median"] / 1000.0, 3),
+                     "achieved_at_kernel_us": prof and prof.get("kernel_ns_median") and
+                     round(tot_bytes / len(per) / (prof["kernel_ns_median"] * 1e-9) / 1e9, 1)},
         "event_floor_us": round(floor_us, 3),
         "hbm_TBps": round(achieved / 1000.0, 4),
         "mfma_frac_fp4": round(tot_flops / (tot_us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),
