@@ -3,9 +3,12 @@
 // anything is enqueued, so an error other than MXFP4_EHIP leaves the stream
 // untouched.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "mxfp4.h"
 #include "mx_internal.hpp"
@@ -21,6 +24,9 @@ int fail(int code, const char* fmt, ...) {
   va_end(ap);
   return code;
 }
+
+// the same signature as fail(), for checks that must not touch the message
+int quiet(int code, const char*, ...) { return code; }
 
 int ok() {
   g_err[0] = '\0';
@@ -73,44 +79,46 @@ int check_gemm_shape(int M, int N, int K) {
 
 // Checks a plan against a shape; `mode_matters` is false for the prequant
 // entry point, which ignores the mode field.
-int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters) {
+int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
+               bool report = true) {
+  int (*const bad)(int, const char*, ...) = report ? fail : quiet;
   if (mode_matters && p.mode != MXFP4_MODE_FUSED && p.mode != MXFP4_MODE_PREQUANT)
-    return fail(MXFP4_EINVAL, "plan.mode must be MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT (got %d)", p.mode);
+    return bad(MXFP4_EINVAL, "plan.mode must be MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT (got %d)", p.mode);
   if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
       p.k_steps_per_wave < 1 || p.split_k < 1)
-    return fail(MXFP4_EINVAL, "plan fields must all be >= 1");
+    return bad(MXFP4_EINVAL, "plan fields must all be >= 1");
   if (p.split_reduce != MXFP4_REDUCE_KERNEL && p.split_reduce != MXFP4_REDUCE_LAST_WG &&
       p.split_reduce != MXFP4_REDUCE_ATOMIC)
-    return fail(MXFP4_EINVAL,
+    return bad(MXFP4_EINVAL,
                 "plan.split_reduce must be MXFP4_REDUCE_KERNEL, _LAST_WG or _ATOMIC (got %d)",
                 p.split_reduce);
   if (p.split_k > mx::kMaxLastWgSplit && p.split_reduce == MXFP4_REDUCE_LAST_WG)
-    return fail(MXFP4_EINVAL, "split_reduce LAST_WG supports split_k <= %d (got %d)", mx::kMaxLastWgSplit,
+    return bad(MXFP4_EINVAL, "split_reduce LAST_WG supports split_k <= %d (got %d)", mx::kMaxLastWgSplit,
                 p.split_k);
   const int mode = mode_matters ? p.mode : MXFP4_MODE_PREQUANT;
   if (!mx::gemm_kernel_available(mode, p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave))
-    return fail(MXFP4_ENOTSUP,
+    return bad(MXFP4_ENOTSUP,
                 "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this build",
                 p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
   const int KS = (int)(((long long)K + 127) / 128);
   if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
-    return fail(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal ceil(K/128))",
+    return bad(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal ceil(K/128))",
                 (long long)p.split_k * p.waves_k * p.k_steps_per_wave, KS);
   if (p.waves_n * p.waves_k > mx::kMaxThreads / 64)
-    return fail(MXFP4_EINVAL, "plan has %d wavefronts per workgroup (max %d)", p.waves_n * p.waves_k,
+    return bad(MXFP4_EINVAL, "plan has %d wavefronts per workgroup (max %d)", p.waves_n * p.waves_k,
                 mx::kMaxThreads / 64);
   mx::Plan q = to_internal(p);
   q.mode = mode;
   const mx::GemmGeom g = mx::gemm_geometry(q, M, N, K);
   if (g.lds_total > (size_t)mx::kMaxLds)
-    return fail(MXFP4_EINVAL, "plan needs %zu bytes of LDS (max %d)", g.lds_total, mx::kMaxLds);
+    return bad(MXFP4_EINVAL, "plan needs %zu bytes of LDS (max %d)", g.lds_total, mx::kMaxLds);
   // a dispatch holds at most 2^32 - 1 work-items
   const long long blocks = 8LL * (((long long)g.ngroups * p.split_k + 7) / 8) * g.mgroups;
   if (blocks * g.threads > 0xFFFFFFFFLL)
-    return fail(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", blocks, g.threads);
+    return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", blocks, g.threads);
   if (p.split_k > 1 && p.split_reduce == MXFP4_REDUCE_KERNEL) {
     const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
-    if (n > 0xFFFFFFFFLL - 63) return fail(MXFP4_EINVAL, "split-K reduce grid too large (%lld threads)", n);
+    if (n > 0xFFFFFFFFLL - 63) return bad(MXFP4_EINVAL, "split-K reduce grid too large (%lld threads)", n);
   }
   return MXFP4_OK;
 }
@@ -144,7 +152,97 @@ WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry
   return w;
 }
 
-// Per-shape table for the tuned shapes, heuristic otherwise.
+// Estimated L2-cold microseconds of a plan, a model fitted to L2-cold sweeps
+// of every plan on 20 shapes (M 1..640, N 1024..8192, K 512..16384; the
+// fitted picks are within 7 % of the best plan on each): each workgroup
+// streams its A rows (bf16 when fused, fp4 + scales when pre-quantized) and
+// B columns (fp4 + scales) for its K range at up to 100 GB/s per CU, less
+// with fewer than eight wavefronts, and in fused mode quantizes its A rows
+// (about 2 us per 64 Ki elements); each further 256 workgroups is another
+// round; a split-K adds the reduce launch, its partials and a little per
+// slice; pre-quantized A adds the quantizer launch and its traffic; a small
+// cost per extra K wavefront.
+double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
+  const long long MT = ((long long)M + 15) / 16, NT = ((long long)N + 15) / 16;
+  const long long cols_wg = (long long)p.waves_n * p.n_tiles_per_wave;
+  const long long wgs = ((MT + p.m_blocks - 1) / p.m_blocks) * ((NT + cols_wg - 1) / cols_wg) *
+                        p.split_k;
+  const double rounds = ceil(wgs / 256.0);
+  const double rows = fmin(16.0 * p.m_blocks, (double)M);
+  const double cols = fmin(16.0 * cols_wg, (double)N);
+  const double kel = 128.0 * p.waves_k * p.k_steps_per_wave;
+  const bool fused = p.mode == MXFP4_MODE_FUSED;
+  const double a_bytes = fused ? 2.0 : 17.0 / 32.0;  // per element
+  const double bytes = rows * kel * a_bytes + cols * kel * 17.0 / 32.0;
+  const int waves = p.waves_n * p.waves_k;
+  const double rate = 100000.0 * fmin(1.0, pow(waves / 8.0, 0.75));  // bytes per us
+  double t = rounds * bytes / rate;
+  if (fused) t += 2.0 * rounds * rows * kel / 65536.0;
+  if (p.split_k > 1) t += 2.0 + (double)p.split_k * M * N * 4.0 / 5.0e6 + 0.05 * p.split_k;
+  if (!fused) t += 2.65 + (double)M * K * 2.5 / 5.0e6;
+  t += 0.1 * (p.waves_k - 1);
+  return t;
+}
+
+// The valid plan (reduce kernel for split-K) of least plan_cost; fused before
+// pre-quantized, so ties keep the single-launch plan.
+mxfp4_plan model_plan(int M, int N, int K) {
+  static const int ksw_opts[] = {1, 2, 3, 4, 6, 7, 8, 12, 14, 16};
+  static const int wk_opts[] = {1, 2, 3, 4, 8};
+  const long long KS = ((long long)K + 127) / 128;
+  const long long MT = ((long long)M + 15) / 16, NT = ((long long)N + 15) / 16;
+  mxfp4_plan best = make_plan(MXFP4_MODE_FUSED, 1, 1, 1, 1, 1, (int)KS);
+  double best_t = 1e300;
+  for (int mode : {MXFP4_MODE_FUSED, MXFP4_MODE_PREQUANT})
+    for (int mbw : {1, 2, 4}) {
+      if (mbw > 1 && mbw > MT) continue;
+      for (int ntw : {1, 2})
+        for (int wn = 1; wn <= 8; ++wn) {
+          if ((long long)wn * ntw > NT) continue;
+          for (int wk : wk_opts) {
+            if (wn * wk > mx::kMaxThreads / 64) continue;
+            for (int ksw : ksw_opts) {
+              if (KS % ((long long)wk * ksw)) continue;
+              const mxfp4_plan p =
+                  make_plan(mode, mbw, ntw, wn, wk, ksw, (int)(KS / ((long long)wk * ksw)));
+              if (check_plan(p, M, N, K, true, false) != MXFP4_OK) continue;
+              const double t = plan_cost(p, M, N, K);
+              if (t < best_t) {
+                best_t = t;
+                best = p;
+              }
+            }
+          }
+        }
+    }
+  return best;
+}
+
+// model_plan is a search over about 4,000 candidates; mxfp4_gemm without a plan
+// asks for it on every call, so the last few shapes' picks are kept.
+mxfp4_plan cached_model_plan(int M, int N, int K) {
+  struct Entry {
+    int M, N, K;
+    mxfp4_plan p;
+  };
+  constexpr int kEntries = 64;
+  static std::mutex mu;
+  static Entry cache[kEntries];
+  static int used = 0, next = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].M == M && cache[i].N == N && cache[i].K == K) return cache[i].p;
+  }
+  const mxfp4_plan p = model_plan(M, N, K);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[next] = Entry{M, N, K, p};
+  next = (next + 1) % kEntries;
+  if (used < kEntries) ++used;
+  return p;
+}
+
+// Per-shape table for the tuned shapes, the cost model otherwise.
 mxfp4_plan default_plan(int M, int N, int K) {
   struct Row {
     int M, N, K;
@@ -164,39 +262,7 @@ mxfp4_plan default_plan(int M, int N, int K) {
   for (const Row& r : table)
     if (r.M == M && r.N == N && r.K == K) return r.p;
 
-  // Heuristic, from the sweeps over the tuned shapes: fused quantization,
-  // one 16-row block per workgroup (row groups of one column task share B in
-  // one XCD's L2), four wavefronts along N, the largest compiled step count
-  // per wavefront that divides the K steps (at most 16), then up to two
-  // wavefronts along K inside the workgroup and the rest as workgroups along
-  // K summed by the reduce kernel.
-  const int KS = (int)(((long long)K + 127) / 128);
-  const int NT = (int)(((long long)N + 15) / 16);
-  static const int ksw_opts[] = {16, 14, 12, 8, 7, 6, 4, 3, 2, 1};
-  int ksw = 1;
-  for (int k : ksw_opts)
-    if (KS % k == 0) {
-      ksw = k;
-      break;
-    }
-  const int rest = KS / ksw;  // split_k * waves_k
-  int wn = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
-  int wk = (rest % 2 == 0) ? 2 : 1;
-  // a grid already wide without K splits keeps K inside the workgroup
-  const long long wide = (((long long)M + 15) / 16) * ((NT + wn - 1) / wn);
-  if (wide >= 512 && rest > 1) {
-    wn = 2;
-    wk = 1;
-    while (wk < 4 && rest % (wk * 2) == 0) wk *= 2;
-  }
-  mxfp4_plan p = make_plan(MXFP4_MODE_FUSED, 1, 1, wn, wk, ksw, rest / wk);
-  // keep the A stage within LDS: trade in-block K waves for workgroups along K
-  while (mx::gemm_geometry(to_internal(p), M, N, K).lds_total > (size_t)mx::kMaxLds &&
-         p.waves_k > 1) {
-    p.waves_k /= 2;
-    p.split_k *= 2;
-  }
-  return p;
+  return cached_model_plan(M, N, K);
 }
 
 int check_workspace(const void* workspace, size_t have, size_t need) {
