@@ -194,3 +194,25 @@ def test_default_plans_are_valid(lib):
         if p.mode == mx.MODE_PREQUANT or p.split_k > 1:
             assert ws > 0
         assert ws == mx.workspace_bytes(M, N, K)
+
+
+def test_default_plans_valid_on_random_shapes(lib):
+    """The plan search returns a plan the plan rules accept for any shape a
+    plan exists for: random M, N, K over the ranges callers use, plus shapes
+    near the size limits where grids and the reduce kernel's thread count
+    rule candidates out."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    shapes = [(int(rng.integers(1, 4097)), int(rng.integers(1, 65537)), 32 * int(rng.integers(1, 1025)))
+              for _ in range(300)]
+    shapes += [(1 << 17, 1 << 17, 256), (1, 1 << 30, 1024), (1 << 24, 16, 65536), (3, 7, 2080)]
+    # a 2^20 x 2^20 C needs more than 2^32 - 1 work-items in every plan (one
+    # lane covers at most one 16-row block of one column): refused, not launched
+    with pytest.raises(mx.Mxfp4Error, match="grid too large"):
+        mx.check_plan(mx.default_plan(1 << 20, 1 << 20, 32), 1 << 20, 1 << 20, 32)
+    for M, N, K in shapes:
+        p = mx.default_plan(M, N, K)
+        mx.check_plan(p, M, N, K)
+        assert p.split_k * p.waves_k * p.k_steps_per_wave == -(-K // 128), (M, N, K, p)
+        assert mx.workspace_bytes(M, N, K) == mx.workspace_bytes(M, N, K, p)
+        assert mx.default_plan(M, N, K) == p  # cached pick is the same
