@@ -162,6 +162,16 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
   };
   uint4 araw[kAPT];
   if constexpr (MODE == 1) {
+    // Rests past the first round (plans whose A stage exceeds kAPT chunks
+    // per wavefront) are loaded and quantized first, round by round, so that
+    // no load is ever issued after the B loads: a load younger than B would
+    // make every later wait for it a wait for all of B.
+    for (int r0 = (nwaves + wave) * kRestsPerRound; r0 < n_rests; r0 += nwaves * kRestsPerRound) {
+#pragma unroll
+      for (int i = 0; i < kRestsPerRound; ++i) load_rest(rest_info(r0 + i), araw + 4 * i);
+#pragma unroll
+      for (int i = 0; i < kRestsPerRound; ++i) quantize_rest(r0 + i, rest_info(r0 + i), araw + 4 * i);
+    }
 #pragma unroll
     for (int i = 0; i < kRestsPerRound; ++i)
       load_rest(rest_info(wave * kRestsPerRound + i), araw + 4 * i);
@@ -210,13 +220,6 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < kRestsPerRound; ++i) {
       const int rest = wave * kRestsPerRound + i;
       quantize_rest(rest, rest_info(rest), araw + 4 * i);
-    }
-    // further rounds (plans whose A stage exceeds kAPT chunks per wavefront)
-    for (int r0 = (nwaves + wave) * kRestsPerRound; r0 < n_rests; r0 += nwaves * kRestsPerRound) {
-#pragma unroll
-      for (int i = 0; i < kRestsPerRound; ++i) load_rest(rest_info(r0 + i), araw + 4 * i);
-#pragma unroll
-      for (int i = 0; i < kRestsPerRound; ++i) quantize_rest(r0 + i, rest_info(r0 + i), araw + 4 * i);
     }
   } else {
     __builtin_amdgcn_s_waitcnt(0);  // the LDS-direct copies
