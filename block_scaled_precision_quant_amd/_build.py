@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4.so")
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_tiled.hip", "api.cpp"]
 HEADERS = ["mx_device.hpp", "mx_internal.hpp"]
 ARCH = "gfx950"
 

@@ -78,12 +78,22 @@ int check_gemm_shape(int M, int N, int K) {
 }
 
 // Checks a plan against a shape; `mode_matters` is false for the prequant
-// entry point, which ignores the mode field.
+// entry point, where the mode only selects the tiled kernel or not.
 int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
                bool report = true) {
   int (*const bad)(int, const char*, ...) = report ? fail : quiet;
-  if (mode_matters && p.mode != MXFP4_MODE_FUSED && p.mode != MXFP4_MODE_PREQUANT)
-    return bad(MXFP4_EINVAL, "plan.mode must be MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT (got %d)", p.mode);
+  if (mode_matters && p.mode != MXFP4_MODE_FUSED && p.mode != MXFP4_MODE_PREQUANT &&
+      p.mode != MXFP4_MODE_TILED)
+    return bad(MXFP4_EINVAL,
+               "plan.mode must be MXFP4_MODE_FUSED, MXFP4_MODE_PREQUANT or MXFP4_MODE_TILED (got %d)",
+               p.mode);
+  if (p.mode == MXFP4_MODE_TILED) {
+    // fixed tiling: the other fields are not used
+    const mx::TiledGeom t = mx::tiled_geometry(M, N, K);
+    if (t.grid * t.threads > 0xFFFFFFFFLL)
+      return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", t.grid, t.threads);
+    return MXFP4_OK;
+  }
   if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
       p.k_steps_per_wave < 1 || p.split_k < 1)
     return bad(MXFP4_EINVAL, "plan fields must all be >= 1");
@@ -137,6 +147,10 @@ struct WsLayout {
 
 WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
   WsLayout w = {0, 0, 0, false};
+  if (p.mode == MXFP4_MODE_TILED) {
+    if (!prequant_entry) w.a = round_up(mxfp4_packed_bytes(M, K), 256);
+    return w;
+  }
   const bool split = p.split_k > 1;
   if (split && p.split_reduce != MXFP4_REDUCE_KERNEL) {
     const mx::GemmGeom g = mx::gemm_geometry(to_internal(p), M, N, K);
@@ -380,7 +394,7 @@ size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan* plan, int M, int N, int
 size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
   if (check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
   mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
-  p.mode = MXFP4_MODE_PREQUANT;
+  if (p.mode != MXFP4_MODE_TILED) p.mode = MXFP4_MODE_PREQUANT;
   if (check_plan(p, M, N, K, false) != MXFP4_OK) return 0;
   return ws_layout(p, M, N, K, true).total();
 }
@@ -413,11 +427,17 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const void* a_src = a;
-  if (p.mode == MXFP4_MODE_PREQUANT) {
+  if (p.mode == MXFP4_MODE_PREQUANT || p.mode == MXFP4_MODE_TILED) {
     mx::launch_quant_packed(a, M, K, lda, ws + wl.a_off(), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "quant_a_packed launch");
     a_src = ws + wl.a_off();
+  }
+  if (p.mode == MXFP4_MODE_TILED) {
+    hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_src),
+                                         static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
+    return ok();
   }
   hipError_t e = mx::launch_gemm(to_internal(p), a_src, lda, static_cast<const uint8_t*>(b_packed), c,
                                  ldc, M, N, K, reinterpret_cast<float*>(ws + wl.part_off()),
@@ -451,11 +471,18 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
   if (b_packed_bytes < bneed)
     return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
   mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
-  p.mode = MXFP4_MODE_PREQUANT;
+  if (p.mode != MXFP4_MODE_TILED) p.mode = MXFP4_MODE_PREQUANT;
   if ((rc = check_plan(p, M, N, K, false))) return rc;
   const WsLayout wl = ws_layout(p, M, N, K, true);
   if ((rc = check_workspace(workspace, workspace_bytes, wl.total()))) return rc;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (p.mode == MXFP4_MODE_TILED) {
+    hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_packed),
+                                         static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
+    return ok();
+  }
   hipError_t e = mx::launch_gemm(to_internal(p), a_packed, 0, static_cast<const uint8_t*>(b_packed), c,
                                  ldc, M, N, K, reinterpret_cast<float*>(ws + wl.part_off()),
                                  reinterpret_cast<unsigned*>(ws), static_cast<hipStream_t>(stream));

@@ -128,16 +128,25 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * mode FUSED quantizes the workgroup's A rows inside the GEMM kernel; mode
  * PREQUANT first runs the quantizer once into the workspace (MX-packed) and
  * the GEMM kernel reads fp4 A.
+ *
+ * mode TILED is the large-M kernel: like PREQUANT it quantizes A into the
+ * workspace first, then one workgroup of four wavefronts computes each
+ * 256 x 256 tile of C over the whole of K with the gfx950 block-scaled
+ * 32x32x64 FP4 instruction (the same products and fp32 sums per output as
+ * the other modes, in K order; results agree with them within fp32
+ * rounding, not bit for bit).  Its tiling is fixed: every other plan field
+ * is ignored.  It pays off when M and N give many 256 x 256 tiles.
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1
 #define MXFP4_MODE_PREQUANT 2
+#define MXFP4_MODE_TILED 3
 
 #define MXFP4_REDUCE_KERNEL 0
 #define MXFP4_REDUCE_LAST_WG 1
 #define MXFP4_REDUCE_ATOMIC 2
 
 typedef struct mxfp4_plan {
-    int mode;             /* MXFP4_MODE_FUSED or MXFP4_MODE_PREQUANT */
+    int mode;             /* MXFP4_MODE_FUSED, _PREQUANT or _TILED */
     int m_blocks;         /* 16-row blocks of A per workgroup: 1, 2 or 4 */
     int n_tiles_per_wave; /* 16-column tiles of B per wavefront: 1 or 2 */
     int waves_n;          /* wavefronts along N per workgroup */
@@ -162,7 +171,8 @@ int mxfp4_check_plan(const mxfp4_plan *plan, int M, int N, int K);
  * with each part rounded up to 256 bytes: tile counters (4 bytes per
  * workgroup tile) when split_k > 1 and split_reduce is LAST_WG or ATOMIC;
  * split_k*M*N*4 bytes of partials when split_k > 1 (M*N*4 bytes, one
- * accumulator, for ATOMIC); the MX-packed A in PREQUANT mode.
+ * accumulator, for ATOMIC); the MX-packed A in PREQUANT and TILED mode
+ * (TILED needs nothing else).
  * 0 when none is needed or the plan is invalid. */
 size_t mxfp4_plan_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);
 
@@ -203,9 +213,11 @@ size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N,
 
 /* GEMM on an A that is already MX-packed (from mxfp4_quant_a_packed), for
  * callers that quantize one activation once and use it against several
- * weights.  The plan's mode is ignored (the kernel reads fp4 A); NULL plan =
- * the default plan's tiling.  Workspace: as for mxfp4_gemm_ex with the plan in
- * PREQUANT mode, minus the MX-packed A part (tile counters, then partials).
+ * weights.  Plan mode MXFP4_MODE_TILED runs the tiled kernel (no workspace);
+ * any other mode value means the plan's tiling with fp4 A, as in PREQUANT
+ * mode.  NULL plan = the default plan.  Workspace: as for mxfp4_gemm_ex with
+ * the plan in PREQUANT mode, minus the MX-packed A part (tile counters, then
+ * partials).
  * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
 int mxfp4_gemm_prequant(const void *a_packed, size_t a_packed_bytes, const void *b_packed,
                         size_t b_packed_bytes, uint16_t *c, int ldc, int M, int N, int K,

@@ -88,7 +88,8 @@ def test_plan_checks(lib):
         return lib.mxfp4_check_plan(ctypes.byref(plan._c()), m, n, k)
 
     assert check(mx.Plan(mx.MODE_PREQUANT, 4, 1, 2, 1, 16, 1)) == 0
-    assert check(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
+    assert check(mx.Plan(4, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
+    assert check(mx.Plan(0, 4, 1, 2, 1, 16, 1)) == EINVAL       # mode
     assert check(mx.Plan(1, 3, 1, 2, 1, 16, 1)) == ENOTSUP      # m_blocks
     assert check(mx.Plan(1, 4, 1, 2, 1, 5, 1)) == ENOTSUP       # k_steps_per_wave
     assert check(mx.Plan(1, 4, 1, 2, 1, 8, 1)) == EINVAL        # covers 8 of 16 steps
@@ -115,6 +116,24 @@ def test_plan_checks(lib):
                  m=1 << 17, n=1 << 17, k=256) == 0
 
 
+def test_tiled_plan(lib):
+    # the tiled mode has a fixed tiling: the other fields are not checked
+    M, N, K = 300, 520, 640
+    for fields in [(1, 1, 1, 1, 1, 1), (0, 0, 0, 0, 0, 0), (3, 7, 99, -1, 5, 2)]:
+        p = mx.Plan(mx.MODE_TILED, *fields, 9)
+        assert lib.mxfp4_check_plan(ctypes.byref(p._c()), M, N, K) == 0
+        # workspace: the MX-packed A only, nothing to zero-fill; none when A
+        # comes pre-quantized
+        assert mx.workspace_bytes(M, N, K, p) == (mx.packed_bytes(M, K) + 255) // 256 * 256
+        assert mx.workspace_zero_bytes(M, N, K, p) == 0
+        assert mx.prequant_workspace_bytes(M, N, K, p) == 0
+    # 2^20 x 2^20 is 2^24 tiles of 256 threads: one more than a dispatch holds
+    p = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 20, 128) == EINVAL
+    assert "grid too large" in mx.load().mxfp4_last_error().decode()
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 20) - 256, 128) == 0
+
+
 @no_gpu
 def test_gemm_rejects_bad_workspace(lib):
     f = lib.mxfp4_gemm_ex
@@ -131,7 +150,10 @@ def test_gemm_rejects_bad_workspace(lib):
     assert call(good, None, 0) == ENULL                     # workspace required
     assert call(good, FAKE, need - 1) == EWORKSPACE
     assert call(good, ctypes.c_void_p(0x10010), need) == EINVAL  # 256-byte alignment
-    assert call(mx.Plan(3, 4, 1, 2, 1, 16, 1)) == EINVAL       # an invalid plan is refused
+    assert call(mx.Plan(4, 4, 1, 2, 1, 16, 1)) == EINVAL       # an invalid plan is refused
+    tiled = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
+    assert call(tiled, None, 0) == ENULL                    # tiled: A is quantized into it
+    assert call(tiled, FAKE, need - 1) == EWORKSPACE
     split = mx.Plan(mx.MODE_FUSED, 1, 1, 1, 1, 4, 4, mx.REDUCE_LAST_WG)
     assert call(split, FAKE, 256 + 4 * M * N * 4 - 4) == EWORKSPACE
 

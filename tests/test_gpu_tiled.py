@@ -1,0 +1,100 @@
+"""The tiled large-M kernel (plan mode MXFP4_MODE_TILED) against the oracle,
+through the C ABI.
+
+Same bar as the other GEMM parity tests: |C_gpu - C_ref| <= 1e-2*|C_ref| + 1e-2
+elementwise.  Shapes cover one 256 x 256 tile, ragged M and N edges inside a
+tile, K that ends inside a 128-element step, grids whose tile count is not a
+multiple of the 8 XCD slots (some workgroups have no tile), and sampled
+outputs of large shapes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_precision_quant_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import block_scaled_precision_quant_amd as mx  # noqa: E402
+from gpu_util import assert_close_to_oracle, bf16_out_to_f32, to_dev_bf16, to_dev_u8  # noqa: E402
+from test_gpu_gemm import reference, run_gemm  # noqa: E402
+
+TILED = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (256, 256, 128),    # one tile, one K step
+    (1, 16, 32),        # one row, one column tile, one K group
+    (300, 520, 640),    # ragged M and N; 5 K steps
+    (257, 272, 160),    # one row past a tile; K ends inside the second step
+    (768, 768, 256),    # 9 tiles: 16 workgroup slots, 7 without a tile
+    (513, 1000, 1504),  # N not a multiple of 16, K = 11.75 steps
+    (2048, 1040, 2080),
+])
+def test_tiled_full_oracle(M, N, K):
+    print("case tiled", M, N, K, flush=True)
+    ref = reference((M, N, K, M * 7 + N))
+    assert_close_to_oracle(run_gemm(ref, TILED), ref["c32"], "tiled %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("name", ["m256_n3072_k1536", "m64_n7168_k2048", "m16_n2112_k7168"])
+def test_tiled_workloads(name):
+    print("case tiled", name, flush=True)
+    ref = reference(name)
+    assert_close_to_oracle(run_gemm(ref, TILED), ref["c32"], "tiled " + name)
+
+
+def test_tiled_prequant_entry_and_repeat():
+    """gemm_prequant with a tiled plan equals the fused-entry tiled call bit
+    for bit (same packed A, same kernel), and a second call repeats it."""
+    M, N, K = 520, 300, 1024
+    ref = reference((M, N, K, 11))
+    a = to_dev_bf16(ref["a_bits"])
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    ap = mx.quant_a_packed(a)
+    c1 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=TILED)
+    c2 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=TILED)
+    c3 = mx.gemm(a, b_packed, N, plan=TILED)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bf16_out_to_f32(c1), ref["c32"], "tiled gemm_prequant")
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    assert torch.equal(c1.view(torch.int16), c3.view(torch.int16))
+
+
+def test_tiled_strided_output():
+    """ldc > N: only the M x N block of C is written."""
+    M, N, K = 260, 200, 384
+    ref = reference((M, N, K, 5))
+    a = to_dev_bf16(ref["a_bits"])
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    big = torch.full((M + 3, N + 37), 7.0, dtype=torch.bfloat16, device=a.device)
+    view = big[:M, :N]
+    mx.gemm(a, b_packed, N, out=view, plan=TILED)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bf16_out_to_f32(view), ref["c32"], "tiled ldc")
+    assert bool((big[:, N:] == 7.0).all()) and bool((big[M:, :] == 7.0).all())
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 8192, 8192), (4096, 4096, 1024), (8200, 2056, 512)])
+def test_tiled_large_sampled(M, N, K):
+    print("case tiled sampled", M, N, K, flush=True)
+    a, b = inputs.make_shape(M, N, K, seed=(M * 13 + N) % 1000)
+    aq, asc = oracle.quantize(a)
+    bq, bsc = oracle.quantize(b)
+    dev_a = to_dev_bf16(a)
+    b_packed = mx.pack_b(to_dev_u8(bq), to_dev_u8(bsc))
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev_a.device)
+    mx.gemm(dev_a, b_packed, N, out=c, plan=TILED)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K)
+    # the first and last rows and columns of tiles, and random ones
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1, M // 2], rng.integers(0, M, 11)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1, N // 2], rng.integers(0, N, 61)]))
+    ad = oracle.dequantize(aq[rows], asc[rows])
+    bd = oracle.dequantize(bq[cols], bsc[cols])
+    want, _ = oracle.gemm(ad, bd, want64=False)
+    r = torch.as_tensor(rows, device=c.device)
+    q = torch.as_tensor(cols, device=c.device)
+    assert_close_to_oracle(bf16_out_to_f32(c[r][:, q]), want, "tiled %dx%dx%d sampled" % (M, N, K))
+    assert not torch.isnan(c).any().item()
