@@ -89,6 +89,8 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
                p.mode);
   if (p.mode == MXFP4_MODE_TILED) {
     // fixed tiling: the other fields are not used
+    if (K > mx::kTiledMaxK)
+      return bad(MXFP4_EINVAL, "MXFP4_MODE_TILED supports K <= %d (got %d)", mx::kTiledMaxK, K);
     const mx::TiledGeom t = mx::tiled_geometry(M, N, K);
     if (t.grid * t.threads > 0xFFFFFFFFLL)
       return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", t.grid, t.threads);

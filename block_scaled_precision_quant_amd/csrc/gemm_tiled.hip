@@ -6,12 +6,13 @@
 // its 256 accumulators and the staged loads in registers) using the 32x32x64
 // block-scaled FP4 instruction, which does twice the work per operand byte of
 // the 16x16x128 one.  K advances one 128-element step at a time through a
-// two-stage LDS ring: the loads of step j + 1 go out into registers before
-// the products of step j and are written to the other stage after them, so
-// one barrier per step suffices and no global load is outstanding at it.
-// (Loads straight to LDS would make the compiler wait for the next step's
-// copy before every read of the current one.)  Each wavefront's operands are
-// gathered from the packed blocks with per-lane LDS addresses:
+// two-stage LDS ring fed from two register sets: a step's global loads are
+// issued two steps before its products and written to LDS after the products
+// of the step before it, so one barrier per step suffices and the loads have
+// two steps' worth of products to arrive.  (Loads straight to LDS would make
+// the compiler wait for the next step's copy before every read of the
+// current one.)  Each wavefront's operands are gathered from the packed
+// blocks with per-lane LDS addresses:
 //
 //   32x32x64 lane L, K half h of the step (elements 64h .. 64h+63):
 //     A row 32u + L%32  ->  16-row tile 2u + (L/16)%2, packed lane
@@ -19,12 +20,15 @@
 //   B column likewise; the scale byte of that (row, K-group) is byte j%4 of
 //   the packed scale dword of the same tile and packed lane.
 //
-//   Result register i of lane L: row 8*(i/4) + 4*(L/32) + i%4, column L%32.
+//   B is the instruction's first operand, so result register i of lane L
+//   holds row L%32 and column 8*(i/4) + 4*(L/32) + i%4: four neighbouring
+//   columns per register group, stored as one 8-byte write.
 //
 // Rows past M and columns past N read clamped (valid) tiles and are never
 // stored.  Workgroup ids go to the 8 XCDs in turn; each XCD takes a
-// contiguous range of tiles in row-major order, so the workgroups of one XCD
-// share A rows in its L2.
+// contiguous range of tiles, ordered in groups of four tile rows walked
+// column by column, so the workgroups running together on one XCD cover a
+// compact block of C and share both A rows and B columns in its L2.
 #include <atomic>
 
 #include "mx_internal.hpp"
@@ -42,6 +46,9 @@ constexpr int kStageAS = 32 * 1024;
 constexpr int kStageBS = 36 * 1024;
 constexpr int kStageBytes = 40 * 1024;
 constexpr int kTiledLds = 2 * kStageBytes;
+// tile order: groups of kGroupM tile rows, column-major inside a group, so
+// the tiles that run at the same time on one XCD form a compact block
+constexpr int kGroupM = 4;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -53,6 +60,23 @@ struct TiledArgs {
   int MT, NT, KS, KG;  // A row tiles, B row tiles, K steps, scale dwords per lane
   int tiles_m, tiles_n, per_xcd;
 };
+
+// Raw buffer access: descriptor word 3 for untyped dword access on CDNA3/4;
+// reads past num_records return zero.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ inline BufRsrc make_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kBufWord3);
+}
+__device__ inline uint4 load16(BufRsrc r, int voff, int soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint32_t load4(BufRsrc r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 
 __device__ inline f32x16 mfma32_fp4(uint4 a, uint4 b, f32x16 acc, int sa, int sb) {
   i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -73,8 +97,12 @@ void gemm_tiled_kernel(TiledArgs g) {
   const int k = blockIdx.x >> 3;
   const int tile = xcd * g.per_xcd + k;
   if (k >= g.per_xcd || tile >= g.tiles_m * g.tiles_n) return;
-  const int tm = tile / g.tiles_n;
-  const int tn = tile - tm * g.tiles_n;
+  const int group = tile / (kGroupM * g.tiles_n);
+  const int first_m = group * kGroupM;
+  const int rows_in = min(kGroupM, g.tiles_m - first_m);
+  const int in_group = tile - group * kGroupM * g.tiles_n;
+  const int tm = first_m + in_group % rows_in;
+  const int tn = in_group / rows_in;
   const int t_a0 = tm * (kTileM / 16);  // first 16-row tile of A
   const int t_b0 = tn * (kTileN / 16);  // first 16-row tile of B
 
@@ -84,46 +112,68 @@ void gemm_tiled_kernel(TiledArgs g) {
   // One step's blocks pass through registers: wavefront w moves blocks w,
   // w + 4, w + 8 and w + 12 of A and of B (1 KiB each) and the scale dwords
   // of the same tiles (256 B each); tiles past the operand's last are
-  // clamped.  Block addresses are wave-uniform, plus one per-lane offset.
+  // clamped.  Two register sets (x and y) alternate, so a step's loads are
+  // issued two steps before its products.  Named registers rather than
+  // arrays: arrays captured by helpers were placed in scratch memory.
+  //
+  // Loads go through buffer descriptors that cover just this workgroup's
+  // tiles (offsets from the first tile fit in 32 bits for K <= 2^22), so an
+  // address is one per-lane constant plus a wave-uniform offset.
+  const int a_tiles = min(kTileM / 16, g.MT - t_a0);
+  const int b_tiles = min(kTileN / 16, g.NT - t_b0);
   const size_t a_sc = da.data_bytes(), b_sc = db.data_bytes();
-  // (named registers rather than arrays: arrays captured by the helpers
-  // below were placed in scratch memory)
-  uint4 na0, na1, na2, na3, nb0, nb1, nb2, nb3;
-  uint32_t nsa0, nsa1, nsa2, nsa3, nsb0, nsb1, nsb2, nsb3;
-#define MX_STAGE_LOAD(R, j)                                                                      \
+  const BufRsrc ra = make_rsrc(g.ap + (size_t)t_a0 * g.KS * kBlockBytes, a_tiles * g.KS * kBlockBytes);
+  const BufRsrc rb = make_rsrc(g.bp + (size_t)t_b0 * g.KS * kBlockBytes, b_tiles * g.KS * kBlockBytes);
+  const BufRsrc ras = make_rsrc(g.ap + a_sc + (size_t)t_a0 * g.KG * 256, a_tiles * g.KG * 256);
+  const BufRsrc rbs = make_rsrc(g.bp + b_sc + (size_t)t_b0 * g.KG * 256, b_tiles * g.KG * 256);
+  const int lane16 = lane * 16, lane4 = lane * 4;
+  uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+  uint32_t xsa0, xsa1, xsa2, xsa3, xsb0, xsb1, xsb2, xsb3;
+  uint4 ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3;
+  uint32_t ysa0, ysa1, ysa2, ysa3, ysb0, ysb1, ysb2, ysb3;
+#define MX_STAGE_LOAD(S, R, j)                                                                   \
   {                                                                                              \
     const int blk = wave + 4 * R;                                                                \
-    const int ta = min(t_a0 + blk, g.MT - 1);                                                    \
-    const int tb = min(t_b0 + blk, g.NT - 1);                                                    \
-    na##R = *reinterpret_cast<const uint4*>(g.ap + ((size_t)ta * g.KS + (j)) * kBlockBytes +     \
-                                            lane * 16);                                          \
-    nb##R = *reinterpret_cast<const uint4*>(g.bp + ((size_t)tb * g.KS + (j)) * kBlockBytes +     \
-                                            lane * 16);                                          \
-    nsa##R = *reinterpret_cast<const uint32_t*>(                                                 \
-        g.ap + a_sc + ((size_t)ta * g.KG + ((j) >> 2)) * 256 + lane * 4);                        \
-    nsb##R = *reinterpret_cast<const uint32_t*>(                                                 \
-        g.bp + b_sc + ((size_t)tb * g.KG + ((j) >> 2)) * 256 + lane * 4);                        \
+    const int ta = min(blk, a_tiles - 1);                                                        \
+    const int tb = min(blk, b_tiles - 1);                                                        \
+    S##a##R = load16(ra, lane16, (ta * g.KS + (j)) * kBlockBytes);                               \
+    S##b##R = load16(rb, lane16, (tb * g.KS + (j)) * kBlockBytes);                               \
+    S##sa##R = load4(ras, lane4, (ta * g.KG + ((j) >> 2)) * 256);                                \
+    S##sb##R = load4(rbs, lane4, (tb * g.KG + ((j) >> 2)) * 256);                                \
   }
-#define MX_STAGE_STORE(R, base)                                                                  \
+#define MX_STAGE_STORE(S, R, base)                                                               \
   {                                                                                              \
     const int blk = wave + 4 * R;                                                                \
-    *reinterpret_cast<uint4*>(base + kStageA + blk * 1024 + lane * 16) = na##R;                  \
-    *reinterpret_cast<uint4*>(base + kStageB + blk * 1024 + lane * 16) = nb##R;                  \
-    *reinterpret_cast<uint32_t*>(base + kStageAS + blk * 256 + lane * 4) = nsa##R;               \
-    *reinterpret_cast<uint32_t*>(base + kStageBS + blk * 256 + lane * 4) = nsb##R;               \
+    *reinterpret_cast<uint4*>(base + kStageA + blk * 1024 + lane * 16) = S##a##R;                \
+    *reinterpret_cast<uint4*>(base + kStageB + blk * 1024 + lane * 16) = S##b##R;                \
+    *reinterpret_cast<uint32_t*>(base + kStageAS + blk * 256 + lane * 4) = S##sa##R;             \
+    *reinterpret_cast<uint32_t*>(base + kStageBS + blk * 256 + lane * 4) = S##sb##R;             \
   }
-  auto load = [&](int j) {
-    MX_STAGE_LOAD(0, j)
-    MX_STAGE_LOAD(1, j)
-    MX_STAGE_LOAD(2, j)
-    MX_STAGE_LOAD(3, j)
+  auto load_x = [&](int j) {
+    MX_STAGE_LOAD(x, 0, j)
+    MX_STAGE_LOAD(x, 1, j)
+    MX_STAGE_LOAD(x, 2, j)
+    MX_STAGE_LOAD(x, 3, j)
   };
-  auto store = [&](int st) {
+  auto load_y = [&](int j) {
+    MX_STAGE_LOAD(y, 0, j)
+    MX_STAGE_LOAD(y, 1, j)
+    MX_STAGE_LOAD(y, 2, j)
+    MX_STAGE_LOAD(y, 3, j)
+  };
+  auto store_x = [&](int st) {
     uint8_t* base = smem + st * kStageBytes;
-    MX_STAGE_STORE(0, base)
-    MX_STAGE_STORE(1, base)
-    MX_STAGE_STORE(2, base)
-    MX_STAGE_STORE(3, base)
+    MX_STAGE_STORE(x, 0, base)
+    MX_STAGE_STORE(x, 1, base)
+    MX_STAGE_STORE(x, 2, base)
+    MX_STAGE_STORE(x, 3, base)
+  };
+  auto store_y = [&](int st) {
+    uint8_t* base = smem + st * kStageBytes;
+    MX_STAGE_STORE(y, 0, base)
+    MX_STAGE_STORE(y, 1, base)
+    MX_STAGE_STORE(y, 2, base)
+    MX_STAGE_STORE(y, 3, base)
   };
 #undef MX_STAGE_LOAD
 #undef MX_STAGE_STORE
@@ -131,71 +181,116 @@ void gemm_tiled_kernel(TiledArgs g) {
   const int wm = wave >> 1;  // 0..1: rows 128*wm
   const int wn = wave & 1;   // 0..1: columns 128*wn
   const int half_tile = (lane >> 4) & 1;
+  // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's 128 x 128; B is
+  // the instruction's first operand, so lane L holds row L%32 and columns
+  // 8*(i/4) + 4*(L/32) + i%4 (four neighbours per register group)
   f32x16 acc[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[u][v] = f32x16{};
 
-  load(0);
-  store(0);
-  for (int j = 0; j < g.KS; ++j) {
-    const int st = j & 1;
-    __syncthreads();  // step j is in stage st; every read of stage st ^ 1 is done
-    // the last step loads its own blocks again (in bounds, never stored):
-    // an unconditional load keeps the staging registers out of scratch
-    load(min(j + 1, g.KS - 1));
-    // keep the products of step j between the loads and the stores of step
-    // j + 1, so the wait for those loads falls after the products are issued
-    __builtin_amdgcn_sched_barrier(0);
-
-    const uint8_t* base = smem + st * kStageBytes;
-    const int sbyte = j & 3;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pl = (lane & 15) + 16 * (2 * h + (lane >> 5));  // packed lane
-      uint4 a[4], b[4];
-      int sa[4], sb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 8 * wm + 2 * u + half_tile;
-        a[u] = *reinterpret_cast<const uint4*>(base + kStageA + t * 1024 + pl * 16);
-        sa[u] = base[kStageAS + t * 256 + pl * 4 + sbyte];
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 8 * wn + 2 * v + half_tile;
-        b[v] = *reinterpret_cast<const uint4*>(base + kStageB + t * 1024 + pl * 16);
-        sb[v] = base[kStageBS + t * 256 + pl * 4 + sbyte];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = mfma32_fp4(a[u], b[v], acc[u][v], sa[u], sb[v]);
-      __builtin_amdgcn_sched_barrier(0);  // one half's operands live at a time
-    }
-    // unconditional (a branch here lets the compiler move the products
-    // below the stores): on the last step this rewrites the other stage,
-    // which every wavefront finished reading before this step's barrier
-    __builtin_amdgcn_sched_barrier(0);
-    store(st ^ 1);
+  // the products of the step in stage st, K step j (a macro: the
+  // accumulators captured by a helper were placed in scratch memory)
+#define MX_PRODUCTS(st, j)                                                                       \
+  {                                                                                              \
+    const uint8_t* base = smem + (st) * kStageBytes;                                             \
+    const int sbyte = (j) & 3;                                                                   \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                              \
+      const int pl = (lane & 15) + 16 * (2 * h + (lane >> 5)); /* packed lane */                 \
+      uint4 a[4], b[4];                                                                          \
+      int sa[4], sb[4];                                                                          \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                            \
+        const int t = 8 * wm + 2 * u + half_tile;                                                \
+        a[u] = *reinterpret_cast<const uint4*>(base + kStageA + t * 1024 + pl * 16);             \
+        sa[u] = base[kStageAS + t * 256 + pl * 4 + sbyte];                                       \
+      }                                                                                          \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                            \
+        const int t = 8 * wn + 2 * v + half_tile;                                                \
+        b[v] = *reinterpret_cast<const uint4*>(base + kStageB + t * 1024 + pl * 16);             \
+        sb[v] = base[kStageBS + t * 256 + pl * 4 + sbyte];                                       \
+      }                                                                                          \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                              \
+          _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[u][v] =                              \
+              mfma32_fp4(b[v], a[u], acc[u][v], sb[v], sa[u]);                                   \
+      __builtin_amdgcn_sched_barrier(0); /* one half's operands live at a time */                \
+    }                                                                                            \
   }
 
-  // epilogue: bf16, nearest even; rows >= M and columns >= N are not stored
-  const int row0 = tm * kTileM + 128 * wm + 4 * (lane >> 5);
-  const int col0 = tn * kTileN + 128 * wn + (lane & 31);
+  // Step j uses stage j % 2.  The loads of step j + 2 go out right after
+  // the barrier of step j, into the register set that step j's blocks left;
+  // the blocks of step j + 1 (loaded during step j - 1) are written to the
+  // other stage after step j's products.  One barrier per step: at it,
+  // every wavefront has finished reading the stage about to be rewritten.
+  // Steps past the last load the last step again (in bounds, never used):
+  // unconditional loads keep the register sets out of scratch.  The loop
+  // takes whole pairs of steps (an exit between the two was found to spill
+  // the register sets); an odd last step follows it.
+  const int last = g.KS - 1;
+  load_x(0);
+  load_y(min(1, last));
+  store_x(0);
+  int j = 0;
+  for (; j + 1 < g.KS; j += 2) {
+    __syncthreads();
+    load_x(min(j + 2, last));
+    __builtin_amdgcn_sched_barrier(0);
+    MX_PRODUCTS(0, j)
+    __builtin_amdgcn_sched_barrier(0);
+    store_y(1);
+    __syncthreads();
+    load_y(min(j + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    MX_PRODUCTS(1, j + 1)
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(0);
+  }
+  if (j < g.KS) {  // odd KS: the last step is in stage 0
+    __syncthreads();
+    MX_PRODUCTS(0, j)
+  }
+#undef MX_PRODUCTS
+
+  // epilogue: bf16, nearest even; rows >= M and columns >= N are not
+  // stored.  Four neighbouring columns go out as one 8-byte store when the
+  // whole tile lies inside N and C's rows are 8-byte aligned; otherwise one
+  // element at a time.
+  const int row0 = tm * kTileM + 128 * wm + (lane & 31);
+  const int col0 = tn * kTileN + 128 * wn + 4 * (lane >> 5);
+  const bool vec = (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7) == 0) &&
+                   (tn + 1) * kTileN <= g.N;
+  if (vec) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
+      const int row = row0 + 32 * u;
+      if (row >= g.M) continue;
+      uint16_t* crow = g.c + (size_t)row * g.ldc + col0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int col = col0 + 32 * v;
-      if (col >= g.N) continue;
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = row0 + 32 * u + 8 * (i >> 2) + (i & 3);
-        if (row < g.M) g.c[(size_t)row * g.ldc + col] = f32_to_bf16_rne(acc[u][v][i]);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = f32_to_bf16_rne(acc[u][v][4 * q]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[u][v][4 * q + 1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[u][v][4 * q + 2]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[u][v][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(crow + 32 * v + 8 * q) = make_uint2(lo, hi);
+        }
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = row0 + 32 * u;
+      if (row >= g.M) continue;
+      uint16_t* crow = g.c + (size_t)row * g.ldc;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int col = col0 + 32 * v + 8 * (i >> 2) + (i & 3);
+          if (col < g.N) crow[col] = f32_to_bf16_rne(acc[u][v][i]);
+        }
+    }
+  }
 }
 
 TiledGeom tiled_geometry(int M, int N, int K) {

@@ -65,6 +65,9 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
 
 // Large-M kernel on pre-quantized A (gemm_tiled.hip): 256 x 256 tiles of C,
 // 32x32x64 products, K pipelined through LDS.
+// Longest K of the tiled kernel: its buffer offsets within one workgroup's
+// 16 row tiles stay below 2^31.
+constexpr int kTiledMaxK = 1 << 22;
 struct TiledGeom {
   int tiles_m, tiles_n, per_xcd;
   long long grid;  // workgroups

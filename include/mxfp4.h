@@ -135,7 +135,8 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * 32x32x64 FP4 instruction (the same products and fp32 sums per output as
  * the other modes, in K order; results agree with them within fp32
  * rounding, not bit for bit).  Its tiling is fixed: every other plan field
- * is ignored.  It pays off when M and N give many 256 x 256 tiles.
+ * is ignored; K must be <= 4194304 (2^22).  It pays off when M and N give
+ * many 256 x 256 tiles.
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1
 #define MXFP4_MODE_PREQUANT 2

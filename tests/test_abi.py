@@ -132,6 +132,10 @@ def test_tiled_plan(lib):
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 20, 128) == EINVAL
     assert "grid too large" in mx.load().mxfp4_last_error().decode()
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 20) - 256, 128) == 0
+    # buffer offsets are 32-bit: K is limited to 2^22
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, 1 << 22) == 0
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, (1 << 22) + 32) == EINVAL
+    assert "K <=" in mx.load().mxfp4_last_error().decode()
 
 
 @no_gpu
