@@ -200,8 +200,28 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
   return t;
 }
 
+// Estimated L2-cold microseconds per call of the tiled mode through
+// mxfp4_gemm, fitted to event timings of six shapes from 256x3072x1536 to
+// 8192^3: the quantizer launch (its A traffic at about 3.2 TB/s), then one
+// round per 256 tiles of 256 x 256, each taking about 1.45 us per 128-K step
+// plus 6 us to start and store; 6 us of launch floor.
+double tiled_cost(int M, int N, int K) {
+  const double tiles = ceil(M / 256.0) * ceil(N / 256.0);
+  const double rounds = ceil(tiles / 256.0);
+  return 6.0 + rounds * (1.45 * ceil(K / 128.0) + 6.0) + 2.65 + (double)M * K * 2.5 / 3.2e6;
+}
+
+// plan_cost is relative: it omits the launch floor and, on shapes with
+// hundreds of thousands of products per CU, the issue rate of the
+// 16x16x128 kernels, which peak at about 0.85 PFLOP/s (measured from M=512
+// up).  Against the tiled mode's absolute estimate they count both.
+double absolute_cost(const mxfp4_plan& p, int M, int N, int K) {
+  return 6.3 + fmax(plan_cost(p, M, N, K), 2.0 * M * N * (double)K / 0.85e9);
+}
+
 // The valid plan (reduce kernel for split-K) of least plan_cost; fused before
-// pre-quantized, so ties keep the single-launch plan.
+// pre-quantized, so ties keep the single-launch plan.  Shapes with at least
+// 32 tiles of 256 x 256 also weigh the tiled mode.
 mxfp4_plan model_plan(int M, int N, int K) {
   static const int ksw_opts[] = {1, 2, 3, 4, 6, 7, 8, 12, 14, 16};
   static const int wk_opts[] = {1, 2, 3, 4, 8};
@@ -231,6 +251,12 @@ mxfp4_plan model_plan(int M, int N, int K) {
           }
         }
     }
+  if (ceil(M / 256.0) * ceil(N / 256.0) >= 32) {
+    const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, 1, 1, 1, 1);
+    if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK &&
+        tiled_cost(M, N, K) < absolute_cost(best, M, N, K))
+      return tiled;
+  }
   return best;
 }
 

@@ -239,6 +239,20 @@ def test_default_plans_valid_on_random_shapes(lib):
     for M, N, K in shapes:
         p = mx.default_plan(M, N, K)
         mx.check_plan(p, M, N, K)
-        assert p.split_k * p.waves_k * p.k_steps_per_wave == -(-K // 128), (M, N, K, p)
+        if p.mode != mx.MODE_TILED:  # the tiled mode's tiling is fixed
+            assert p.split_k * p.waves_k * p.k_steps_per_wave == -(-K // 128), (M, N, K, p)
         assert mx.workspace_bytes(M, N, K) == mx.workspace_bytes(M, N, K, p)
         assert mx.default_plan(M, N, K) == p  # cached pick is the same
+
+
+def test_default_plan_mode_by_size(lib):
+    """Small and mid shapes keep the 16x16x128 kernels; shapes with hundreds
+    of 256 x 256 tiles go to the tiled kernel, which measured 2.4-3x faster
+    there (1024x8192x8192 and up)."""
+    for M, N, K in [(4, 2880, 512), (256, 3072, 1536), (512, 7168, 2048), (512, 4096, 4096),
+                    (2048, 2048, 2048), (64, 65536, 4096)]:
+        assert mx.default_plan(M, N, K).mode != mx.MODE_TILED, (M, N, K)
+    for M, N, K in [(1024, 8192, 8192), (2048, 4096, 4096), (4096, 4096, 4096), (8192, 8192, 8192)]:
+        p = mx.default_plan(M, N, K)
+        assert p.mode == mx.MODE_TILED, (M, N, K, p)
+        assert mx.workspace_bytes(M, N, K) == mx.packed_bytes(M, K) + (-mx.packed_bytes(M, K) % 256)
