@@ -190,66 +190,109 @@ void gemm_tiled_kernel(TiledArgs g) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[u][v] = f32x16{};
 
-  // the products of the step in stage st, K step j (a macro: the
-  // accumulators captured by a helper were placed in scratch memory)
-#define MX_PRODUCTS(st, j)                                                                       \
+  // Operands of one half of a K step (64 elements) for the wavefront's
+  // 4 x 4 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
+  // half 0; half 1 is 512 bytes further for codes and 128 for scales, tile
+  // u (or v) 2048 and 512 further, stage 1 kStageBytes further.
+  const int pl0 = (lane & 15) + 16 * (lane >> 5);  // packed lane, K half 0
+  const int off_a = kStageA + (8 * wm + half_tile) * 1024 + pl0 * 16;
+  const int off_b = kStageB + (8 * wn + half_tile) * 1024 + pl0 * 16;
+  const int off_as = kStageAS + (8 * wm + half_tile) * 256 + pl0 * 4;
+  const int off_bs = kStageBS + (8 * wn + half_tile) * 256 + pl0 * 4;
+  uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
+  int psa0, psa1, psa2, psa3, psb0, psb1, psb2, psb3;
+  int qsa0, qsa1, qsa2, qsa3, qsb0, qsb1, qsb2, qsb3;
+#define MX_LDS16(off) (*reinterpret_cast<const uint4*>(smem + (off)))
+  // S = p or q, half h, stage st, scale byte sbyte (K step % 4)
+#define MX_READ(S, st, h, sbyte)                                                                 \
   {                                                                                              \
-    const uint8_t* base = smem + (st) * kStageBytes;                                             \
-    const int sbyte = (j) & 3;                                                                   \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                              \
-      const int pl = (lane & 15) + 16 * (2 * h + (lane >> 5)); /* packed lane */                 \
-      uint4 a[4], b[4];                                                                          \
-      int sa[4], sb[4];                                                                          \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                            \
-        const int t = 8 * wm + 2 * u + half_tile;                                                \
-        a[u] = *reinterpret_cast<const uint4*>(base + kStageA + t * 1024 + pl * 16);             \
-        sa[u] = base[kStageAS + t * 256 + pl * 4 + sbyte];                                       \
-      }                                                                                          \
-      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                            \
-        const int t = 8 * wn + 2 * v + half_tile;                                                \
-        b[v] = *reinterpret_cast<const uint4*>(base + kStageB + t * 1024 + pl * 16);             \
-        sb[v] = base[kStageBS + t * 256 + pl * 4 + sbyte];                                       \
-      }                                                                                          \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                              \
-          _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[u][v] =                              \
-              mfma32_fp4(b[v], a[u], acc[u][v], sb[v], sa[u]);                                   \
-      __builtin_amdgcn_sched_barrier(0); /* one half's operands live at a time */                \
+    const int o = (st) * kStageBytes + (h) * 512;                                                \
+    const int os = (st) * kStageBytes + (h) * 128 + (sbyte);                                     \
+    S##a0 = MX_LDS16(off_a + o);                                                                 \
+    S##a1 = MX_LDS16(off_a + o + 2048);                                                          \
+    S##a2 = MX_LDS16(off_a + o + 4096);                                                          \
+    S##a3 = MX_LDS16(off_a + o + 6144);                                                          \
+    S##b0 = MX_LDS16(off_b + o);                                                                 \
+    S##b1 = MX_LDS16(off_b + o + 2048);                                                          \
+    S##b2 = MX_LDS16(off_b + o + 4096);                                                          \
+    S##b3 = MX_LDS16(off_b + o + 6144);                                                          \
+    S##sa0 = smem[off_as + os];                                                                  \
+    S##sa1 = smem[off_as + os + 512];                                                            \
+    S##sa2 = smem[off_as + os + 1024];                                                           \
+    S##sa3 = smem[off_as + os + 1536];                                                           \
+    S##sb0 = smem[off_bs + os];                                                                  \
+    S##sb1 = smem[off_bs + os + 512];                                                            \
+    S##sb2 = smem[off_bs + os + 1024];                                                           \
+    S##sb3 = smem[off_bs + os + 1536];                                                           \
+  }
+#define MX_ROW(S, u)                                                                             \
+  acc[u][0] = mfma32_fp4(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                            \
+  acc[u][1] = mfma32_fp4(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);                            \
+  acc[u][2] = mfma32_fp4(S##b2, S##a##u, acc[u][2], S##sb2, S##sa##u);                            \
+  acc[u][3] = mfma32_fp4(S##b3, S##a##u, acc[u][3], S##sb3, S##sa##u);
+#define MX_MFMA(S) \
+  { MX_ROW(S, 0) MX_ROW(S, 1) MX_ROW(S, 2) MX_ROW(S, 3) }
+  // one step in stage st (K step j): the loads of step j + 2 into register
+  // set L interleaved with the products of half 0, the blocks of step j + 1
+  // from register set W written to the other stage, the barrier, the half-0
+  // operands of step j + 1 read, the products of half 1, the half-1 operands
+  // of step j + 1 read
+#define MX_STEP(st, j, L, W)                                                                     \
+  {                                                                                              \
+    load_##L(min((j) + 2, last));                                                                \
+    MX_MFMA(p)                                                                                   \
+    store_##W(1 - (st));                                                                         \
+    for (int i = 0; i < 12; ++i) {                                                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                              \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* global load */                       \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); /* LDS write */                         \
     }                                                                                            \
+    for (int i = 0; i < 4; ++i) {                                                                \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
+    }                                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    __syncthreads();                                                                             \
+    MX_READ(p, 1 - (st), 0, ((j) + 1) & 3)                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MX_MFMA(q)                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    MX_READ(q, 1 - (st), 1, ((j) + 1) & 3)                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
   }
 
-  // Step j uses stage j % 2.  The loads of step j + 2 go out right after
-  // the barrier of step j, into the register set that step j's blocks left;
-  // the blocks of step j + 1 (loaded during step j - 1) are written to the
-  // other stage after step j's products.  One barrier per step: at it,
-  // every wavefront has finished reading the stage about to be rewritten.
-  // Steps past the last load the last step again (in bounds, never used):
+  // Step j uses stage j % 2 and runs as one MX_STEP: at its start, its
+  // operands are being read and register set W holds the blocks of step
+  // j + 1 (loaded during step j - 1).  The barrier sits between the two
+  // halves' products; at it every wavefront has finished reading stage
+  // j % 2's operands for step j (the barrier waits for all LDS accesses)
+  // and has written step j + 1's blocks, so the step after next may
+  // overwrite stage j % 2 and step j + 1's operands may be read, while the
+  // products of half 1 keep the matrix cores busy across it.  Steps past
+  // the last load and read the last step again (in bounds, never used):
   // unconditional loads keep the register sets out of scratch.  The loop
-  // takes whole pairs of steps (an exit between the two was found to spill
-  // the register sets); an odd last step follows it.
+  // takes whole pairs of steps; an odd last step follows it.
   const int last = g.KS - 1;
   load_x(0);
   load_y(min(1, last));
   store_x(0);
+  __syncthreads();
+  MX_READ(p, 0, 0, 0)
+  MX_READ(q, 0, 1, 0)
   int j = 0;
   for (; j + 1 < g.KS; j += 2) {
-    __syncthreads();
-    load_x(min(j + 2, last));
-    __builtin_amdgcn_sched_barrier(0);
-    MX_PRODUCTS(0, j)
-    __builtin_amdgcn_sched_barrier(0);
-    store_y(1);
-    __syncthreads();
-    load_y(min(j + 3, last));
-    __builtin_amdgcn_sched_barrier(0);
-    MX_PRODUCTS(1, j + 1)
-    __builtin_amdgcn_sched_barrier(0);
-    store_x(0);
+    MX_STEP(0, j, x, y)
+    MX_STEP(1, j + 1, y, x)
   }
-  if (j < g.KS) {  // odd KS: the last step is in stage 0
-    __syncthreads();
-    MX_PRODUCTS(0, j)
+  if (j < g.KS) {  // odd KS: the last step is in stage 0, its operands read
+    MX_MFMA(p)
+    MX_MFMA(q)
   }
-#undef MX_PRODUCTS
+#undef MX_STEP
+#undef MX_MFMA
+#undef MX_ROW
+#undef MX_READ
+#undef MX_LDS16
 
   // epilogue: bf16, nearest even; rows >= M and columns >= N are not
   // stored.  Four neighbouring columns go out as one 8-byte store when the
