@@ -1,12 +1,14 @@
 // quant.hip -- bf16 -> MXFP4 quantizer kernels and the one-time B repack.
 //
-// Quantizer work unit: one lane takes 8 consecutive bf16 (one 16-byte load);
-// the 4 lanes of an aligned quad cover one 32-element group, find its
-// maximum with two DPP steps, and each lane encodes its 8 elements into one
-// dword of codes.  Loads are coalesced along K (a wave reads 1 KiB of
-// contiguous row data).  Every kernel walks its items with a grid-stride
-// loop, so the grid stays within a dispatch's 2^32 work-items at any size;
-// the stride is a multiple of 256, so quads stay whole.
+// Linear quantizer work unit: one lane takes 8 consecutive bf16 (one
+// 16-byte load); the 4 lanes of an aligned quad cover one 32-element group,
+// find its maximum with two DPP steps, and each lane encodes its 8 elements
+// into one dword of codes.  Loads are coalesced along K (a wave reads 1 KiB
+// of contiguous row data).  The packed quantizer instead gives each lane a
+// whole group, so that its 16 bytes of codes land in packed order.  Every
+// kernel walks its items with a grid-stride loop, so the grid stays within
+// a dispatch's 2^32 work-items at any size; the stride is a multiple of
+// 256, so quads stay whole.
 #include "mx_internal.hpp"
 
 namespace mx {
@@ -40,38 +42,40 @@ __global__ __launch_bounds__(kQuantBlock) void quant_linear_kernel(const uint16_
 }
 
 // MX-packed output, padding included: rows >= M and K-groups >= K/32 get
-// code 0 and scale 127.  One thread per 8-element item of the padded
-// RT*16 x KS*128 matrix.
+// code 0 and scale 127.  One lane per 16-byte chunk of the packed data, in
+// packed order (tile t, step j, packed lane l: row 16t + l%16, 32-group
+// 4j + l/16), so a wavefront writes one whole 1 KiB block: the lane reads
+// its group's 64 bytes, takes the maximum, encodes the 32 values and stores
+// the codes, then the group's scale byte into its dword of the scale part.
 __global__ __launch_bounds__(kQuantBlock) void quant_packed_kernel(const uint16_t* __restrict__ a, int M,
                                                            int K, int lda,
                                                            uint8_t* __restrict__ out,
                                                            PackedDims d) {
-  const int per_row = d.KS * 16;  // 8-element items per padded row
-  const long long n_items = (long long)d.RT * kTileRows * per_row;
+  const long long n_items = (long long)d.RT * d.KS * 64;
   const long long stride = (long long)gridDim.x * blockDim.x;
+  const int groups = K / kGroup;
   for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < n_items;
        it += stride) {
-    const int row = (int)(it / per_row);
-    const int kk = (int)(it % per_row);
-    const int gi = kk >> 2;  // 32-group index along K
-    const int p = kk & 3;    // quarter of the group
-    const int j = gi >> 2;   // 128-K step
-    const int lane = (row & 15) + 16 * (gi & 3);
-    const int t = row >> 4;
-    uint32_t codes = 0, byte = 127;
-    if (row < M && gi < K / kGroup) {  // uniform over the quad (same row and group)
-      const uint4 v = *reinterpret_cast<const uint4*>(a + (size_t)row * lda + (size_t)kk * 8);
-      const uint32_t amax = quad_max(amax8_bits(v));
+    const int l = (int)(it & 63);
+    const int tj = (int)(it >> 6);  // < 2^31: M*K is at most 2^40
+    const int t = tj / d.KS;
+    const int j = tj - t * d.KS;
+    const int row = 16 * t + (l & 15);
+    const int gi = 4 * j + (l >> 4);
+    uint4 codes = {0u, 0u, 0u, 0u};
+    uint32_t byte = 127;
+    if (row < M && gi < groups) {
+      const uint4* src = reinterpret_cast<const uint4*>(a + (size_t)row * lda + (size_t)gi * kGroup);
+      const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      const uint32_t amax = max(max(amax8_bits(v0), amax8_bits(v1)), max(amax8_bits(v2), amax8_bits(v3)));
       byte = scale_byte_from_amax(amax);
-      codes = encode8(v, byte);
+      codes = make_uint4(encode8(v0, byte), encode8(v1, byte), encode8(v2, byte), encode8(v3, byte));
     }
-    *reinterpret_cast<uint32_t*>(out + d.data_off(t, j, lane) + 4 * p) = codes;
-    if (p == 0) {
-      uint8_t* sc = out + d.scale_off(t, j >> 2, lane);
-      sc[j & 3] = (uint8_t)byte;
-      if (j == d.KS - 1) {  // fill the unused steps of the last scale dword
-        for (int s = (j & 3) + 1; s < 4; ++s) sc[s] = 127;
-      }
+    *reinterpret_cast<uint4*>(out + (size_t)it * 16) = codes;
+    uint8_t* sc = out + d.scale_off(t, j >> 2, l);
+    sc[j & 3] = (uint8_t)byte;
+    if (j == d.KS - 1) {  // fill the unused steps of the last scale dword
+      for (int s = (j & 3) + 1; s < 4; ++s) sc[s] = 127;
     }
   }
 }
@@ -139,7 +143,7 @@ void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_
 void launch_quant_packed(const uint16_t* a, int M, int K, int lda, uint8_t* out,
                          hipStream_t stream) {
   const PackedDims d = packed_dims(M, K);
-  const long long n = (long long)d.RT * kTileRows * d.KS * 16;
+  const long long n = (long long)d.RT * d.KS * 64;
   hipLaunchKernelGGL(quant_packed_kernel, dim3(grid_for(n)), dim3(kQuantBlock), 0, stream, a, M, K,
                      lda, out, d);
 }
