@@ -29,8 +29,6 @@
 // contiguous range of tiles, ordered in groups of four tile rows walked
 // column by column, so the workgroups running together on one XCD cover a
 // compact block of C and share both A rows and B columns in its L2.
-#include <atomic>
-
 #include "mx_internal.hpp"
 
 namespace mx {
@@ -45,12 +43,20 @@ constexpr int kStageB = 16 * 1024;
 constexpr int kStageAS = 32 * 1024;
 constexpr int kStageBS = 36 * 1024;
 constexpr int kStageBytes = 40 * 1024;
-constexpr int kTiledLds = 2 * kStageBytes;
 // tile order: groups of kGroupM tile rows, column-major inside a group, so
 // the tiles that run at the same time on one XCD form a compact block
 constexpr int kGroupM = 4;
 
+// The four pipeline stages (160 KiB, all of a CU's LDS), as separate
+// arrays: the compiler then tracks the asynchronous copies into each stage
+// on their own, so a read of one stage waits only for the copies into it.
+__shared__ __align__(16) uint8_t g_stage0[kStageBytes];
+__shared__ __align__(16) uint8_t g_stage1[kStageBytes];
+__shared__ __align__(16) uint8_t g_stage2[kStageBytes];
+__shared__ __align__(16) uint8_t g_stage3[kStageBytes];
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct TiledArgs {
   const uint8_t* ap;  // MX-packed A
@@ -70,24 +76,28 @@ constexpr int kBufWord3 = 0x00020000;
 __device__ inline BufRsrc make_rsrc(const uint8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kBufWord3);
 }
-__device__ inline uint4 load16(BufRsrc r, int voff, int soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// Asynchronous copy global -> LDS: lane L's 16 (or 4) bytes at voff + soff
+// land at lds + 16 L (or 4 L); lds is wave-uniform.
+typedef __attribute__((address_space(3))) void* LdsPtr;
+__device__ inline void dma16(BufRsrc r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, 0);
 }
-__device__ inline uint32_t load4(BufRsrc r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+__device__ inline void dma4(BufRsrc r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 4, voff, soff, 0, 0);
 }
 
+// kSel selects the scale byte of sa and sb (the K step's position in its
+// group of four steps)
+template <int kSel>
 __device__ inline f32x16 mfma32_fp4(uint4 a, uint4 b, f32x16 acc, int sa, int sb) {
   i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   i32x8 b8 = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  // format 4 = e2m1 for both operands; byte 0 of each scale register
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 4, 4, 0, sa, 0, sb);
+  // format 4 = e2m1 for both operands
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 4, 4, kSel, sa, kSel, sb);
 }
 
 __global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiled_kernel(TiledArgs g) {
-  extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,14 +119,10 @@ void gemm_tiled_kernel(TiledArgs g) {
   const PackedDims da = {g.MT, g.KS, g.KG};
   const PackedDims db = {g.NT, g.KS, g.KG};
 
-  // One step's blocks pass through registers: wavefront w moves blocks w,
-  // w + 4, w + 8 and w + 12 of A and of B (1 KiB each) and the scale dwords
-  // of the same tiles (256 B each); tiles past the operand's last are
-  // clamped.  Two register sets (x and y) alternate, so a step's loads are
-  // issued two steps before its products.  Named registers rather than
-  // arrays: arrays captured by helpers were placed in scratch memory.
-  //
-  // Loads go through buffer descriptors that cover just this workgroup's
+  // Copies: wavefront w moves blocks w, w + 4, w + 8 and w + 12 of A and of
+  // B (1 KiB each) and the scale dwords of the same tiles (256 B each) of a
+  // step into that step's stage; tiles past the operand's last are clamped.
+  // They go through buffer descriptors that cover just this workgroup's
   // tiles (offsets from the first tile fit in 32 bits for K <= 2^22), so an
   // address is one per-lane constant plus a wave-uniform offset.
   const int a_tiles = min(kTileM / 16, g.MT - t_a0);
@@ -127,56 +133,28 @@ void gemm_tiled_kernel(TiledArgs g) {
   const BufRsrc ras = make_rsrc(g.ap + a_sc + (size_t)t_a0 * g.KG * 256, a_tiles * g.KG * 256);
   const BufRsrc rbs = make_rsrc(g.bp + b_sc + (size_t)t_b0 * g.KG * 256, b_tiles * g.KG * 256);
   const int lane16 = lane * 16, lane4 = lane * 4;
-  uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
-  uint32_t xsa0, xsa1, xsa2, xsa3, xsb0, xsb1, xsb2, xsb3;
-  uint4 ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3;
-  uint32_t ysa0, ysa1, ysa2, ysa3, ysb0, ysb1, ysb2, ysb3;
-#define MX_STAGE_LOAD(S, R, j)                                                                   \
-  {                                                                                              \
-    const int blk = wave + 4 * R;                                                                \
-    const int ta = min(blk, a_tiles - 1);                                                        \
-    const int tb = min(blk, b_tiles - 1);                                                        \
-    S##a##R = load16(ra, lane16, (ta * g.KS + (j)) * kBlockBytes);                               \
-    S##b##R = load16(rb, lane16, (tb * g.KS + (j)) * kBlockBytes);                               \
-    S##sa##R = load4(ras, lane4, (ta * g.KG + ((j) >> 2)) * 256);                                \
-    S##sb##R = load4(rbs, lane4, (tb * g.KG + ((j) >> 2)) * 256);                                \
+  int sa_[4], sb_[4], ssa_[4], ssb_[4];  // wave-uniform offsets of the wavefront's tiles
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ta = min(wave + 4 * r, a_tiles - 1), tb = min(wave + 4 * r, b_tiles - 1);
+    sa_[r] = ta * g.KS * kBlockBytes;
+    sb_[r] = tb * g.KS * kBlockBytes;
+    ssa_[r] = ta * g.KG * 256;
+    ssb_[r] = tb * g.KG * 256;
   }
-#define MX_STAGE_STORE(S, R, base)                                                               \
+  const int last = g.KS - 1;
+  // copy step jj (clamped to the last) into stage ST
+#define MX_DMA(ST, jj)                                                                           \
   {                                                                                              \
-    const int blk = wave + 4 * R;                                                                \
-    *reinterpret_cast<uint4*>(base + kStageA + blk * 1024 + lane * 16) = S##a##R;                \
-    *reinterpret_cast<uint4*>(base + kStageB + blk * 1024 + lane * 16) = S##b##R;                \
-    *reinterpret_cast<uint32_t*>(base + kStageAS + blk * 256 + lane * 4) = S##sa##R;             \
-    *reinterpret_cast<uint32_t*>(base + kStageBS + blk * 256 + lane * 4) = S##sb##R;             \
+    const int js = min((jj), last);                                                              \
+    const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                              \
+      dma16(ra, ST + kStageA + (wave + 4 * r) * 1024, lane16, sa_[r] + od);                      \
+      dma16(rb, ST + kStageB + (wave + 4 * r) * 1024, lane16, sb_[r] + od);                      \
+      dma4(ras, ST + kStageAS + (wave + 4 * r) * 256, lane4, ssa_[r] + os);                      \
+      dma4(rbs, ST + kStageBS + (wave + 4 * r) * 256, lane4, ssb_[r] + os);                      \
+    }                                                                                            \
   }
-  auto load_x = [&](int j) {
-    MX_STAGE_LOAD(x, 0, j)
-    MX_STAGE_LOAD(x, 1, j)
-    MX_STAGE_LOAD(x, 2, j)
-    MX_STAGE_LOAD(x, 3, j)
-  };
-  auto load_y = [&](int j) {
-    MX_STAGE_LOAD(y, 0, j)
-    MX_STAGE_LOAD(y, 1, j)
-    MX_STAGE_LOAD(y, 2, j)
-    MX_STAGE_LOAD(y, 3, j)
-  };
-  auto store_x = [&](int st) {
-    uint8_t* base = smem + st * kStageBytes;
-    MX_STAGE_STORE(x, 0, base)
-    MX_STAGE_STORE(x, 1, base)
-    MX_STAGE_STORE(x, 2, base)
-    MX_STAGE_STORE(x, 3, base)
-  };
-  auto store_y = [&](int st) {
-    uint8_t* base = smem + st * kStageBytes;
-    MX_STAGE_STORE(y, 0, base)
-    MX_STAGE_STORE(y, 1, base)
-    MX_STAGE_STORE(y, 2, base)
-    MX_STAGE_STORE(y, 3, base)
-  };
-#undef MX_STAGE_LOAD
-#undef MX_STAGE_STORE
 
   const int wm = wave >> 1;  // 0..1: rows 128*wm
   const int wn = wave & 1;   // 0..1: columns 128*wn
@@ -193,7 +171,8 @@ void gemm_tiled_kernel(TiledArgs g) {
   // Operands of one half of a K step (64 elements) for the wavefront's
   // 4 x 4 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
   // half 0; half 1 is 512 bytes further for codes and 128 for scales, tile
-  // u (or v) 2048 and 512 further, stage 1 kStageBytes further.
+  // u (or v) 2048 and 512 further.  The whole scale dword is read; the
+  // instruction picks the step's byte.
   const int pl0 = (lane & 15) + 16 * (lane >> 5);  // packed lane, K half 0
   const int off_a = kStageA + (8 * wm + half_tile) * 1024 + pl0 * 16;
   const int off_b = kStageB + (8 * wn + half_tile) * 1024 + pl0 * 16;
@@ -202,134 +181,153 @@ void gemm_tiled_kernel(TiledArgs g) {
   uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
   int psa0, psa1, psa2, psa3, psb0, psb1, psb2, psb3;
   int qsa0, qsa1, qsa2, qsa3, qsb0, qsb1, qsb2, qsb3;
-#define MX_LDS16(off) (*reinterpret_cast<const uint4*>(smem + (off)))
-  // S = p or q, half h, stage st, scale byte sbyte (K step % 4)
-#define MX_READ(S, st, h, sbyte)                                                                 \
+#define MX_LDS16(ST, off) (*reinterpret_cast<const uint4*>(ST + (off)))
+#define MX_LDS4(ST, off) (*reinterpret_cast<const int*>(ST + (off)))
+  // S = p or q, half h, stage ST
+#define MX_READ(S, ST, h)                                                                        \
   {                                                                                              \
-    const int o = (st) * kStageBytes + (h) * 512;                                                \
-    const int os = (st) * kStageBytes + (h) * 128 + (sbyte);                                     \
-    S##a0 = MX_LDS16(off_a + o);                                                                 \
-    S##a1 = MX_LDS16(off_a + o + 2048);                                                          \
-    S##a2 = MX_LDS16(off_a + o + 4096);                                                          \
-    S##a3 = MX_LDS16(off_a + o + 6144);                                                          \
-    S##b0 = MX_LDS16(off_b + o);                                                                 \
-    S##b1 = MX_LDS16(off_b + o + 2048);                                                          \
-    S##b2 = MX_LDS16(off_b + o + 4096);                                                          \
-    S##b3 = MX_LDS16(off_b + o + 6144);                                                          \
-    S##sa0 = smem[off_as + os];                                                                  \
-    S##sa1 = smem[off_as + os + 512];                                                            \
-    S##sa2 = smem[off_as + os + 1024];                                                           \
-    S##sa3 = smem[off_as + os + 1536];                                                           \
-    S##sb0 = smem[off_bs + os];                                                                  \
-    S##sb1 = smem[off_bs + os + 512];                                                            \
-    S##sb2 = smem[off_bs + os + 1024];                                                           \
-    S##sb3 = smem[off_bs + os + 1536];                                                           \
+    S##a0 = MX_LDS16(ST, off_a + (h) * 512);                                                     \
+    S##a1 = MX_LDS16(ST, off_a + (h) * 512 + 2048);                                              \
+    S##a2 = MX_LDS16(ST, off_a + (h) * 512 + 4096);                                              \
+    S##a3 = MX_LDS16(ST, off_a + (h) * 512 + 6144);                                              \
+    S##b0 = MX_LDS16(ST, off_b + (h) * 512);                                                     \
+    S##b1 = MX_LDS16(ST, off_b + (h) * 512 + 2048);                                              \
+    S##b2 = MX_LDS16(ST, off_b + (h) * 512 + 4096);                                              \
+    S##b3 = MX_LDS16(ST, off_b + (h) * 512 + 6144);                                              \
+    S##sa0 = MX_LDS4(ST, off_as + (h) * 128);                                                    \
+    S##sa1 = MX_LDS4(ST, off_as + (h) * 128 + 512);                                              \
+    S##sa2 = MX_LDS4(ST, off_as + (h) * 128 + 1024);                                             \
+    S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                             \
+    S##sb0 = MX_LDS4(ST, off_bs + (h) * 128);                                                    \
+    S##sb1 = MX_LDS4(ST, off_bs + (h) * 128 + 512);                                              \
+    S##sb2 = MX_LDS4(ST, off_bs + (h) * 128 + 1024);                                             \
+    S##sb3 = MX_LDS4(ST, off_bs + (h) * 128 + 1536);                                             \
   }
-#define MX_ROW(S, u)                                                                             \
-  acc[u][0] = mfma32_fp4(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                            \
-  acc[u][1] = mfma32_fp4(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);                            \
-  acc[u][2] = mfma32_fp4(S##b2, S##a##u, acc[u][2], S##sb2, S##sa##u);                            \
-  acc[u][3] = mfma32_fp4(S##b3, S##a##u, acc[u][3], S##sb3, S##sa##u);
-#define MX_MFMA(S) \
-  { MX_ROW(S, 0) MX_ROW(S, 1) MX_ROW(S, 2) MX_ROW(S, 3) }
-  // one step in stage st (K step j): the loads of step j + 2 into register
-  // set L interleaved with the products of half 0, the blocks of step j + 1
-  // from register set W written to the other stage, the barrier, the half-0
-  // operands of step j + 1 read, the products of half 1, the half-1 operands
-  // of step j + 1 read
-#define MX_STEP(st, j, L, W)                                                                     \
+#define MX_ROW(S, u, k)                                                                          \
+  acc[u][0] = mfma32_fp4<k>(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                        \
+  acc[u][1] = mfma32_fp4<k>(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);                        \
+  acc[u][2] = mfma32_fp4<k>(S##b2, S##a##u, acc[u][2], S##sb2, S##sa##u);                        \
+  acc[u][3] = mfma32_fp4<k>(S##b3, S##a##u, acc[u][3], S##sb3, S##sa##u);
+#define MX_MFMA(S, k) \
+  { MX_ROW(S, 0, k) MX_ROW(S, 1, k) MX_ROW(S, 2, k) MX_ROW(S, 3, k) }
+  // Own copies of step j + 1 done (those of steps j + 2 and j + 3, 32
+  // instructions, may be in flight), own LDS accesses done, then the
+  // workgroup barrier.  An asm statement: the compiler's barrier would wait
+  // for every copy in flight.
+#define MX_BARRIER()                                                                             \
+  __builtin_amdgcn_sched_barrier(0);                                                             \
+  asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");         \
+  __builtin_amdgcn_sched_barrier(0);
+  // K step jj = 4i + k, in stage STC; STN is the stage of step jj + 1:
+  // products of half 0; barrier; the half-0 operands of step jj + 1 read,
+  // the copy of step jj + 4 into STC issued and the products of half 1, all
+  // interleaved; the half-1 operands of step jj + 1 read
+#define MX_STEP(k, jj, STC, STN)                                                                 \
   {                                                                                              \
-    load_##L(min((j) + 2, last));                                                                \
-    MX_MFMA(p)                                                                                   \
-    store_##W(1 - (st));                                                                         \
-    for (int i = 0; i < 12; ++i) {                                                               \
+    MX_MFMA(p, k)                                                                                \
+    MX_BARRIER()                                                                                 \
+    MX_READ(p, STN, 0)                                                                           \
+    MX_DMA(STC, (jj) + 4)                                                                        \
+    MX_MFMA(q, k)                                                                                \
+    for (int i = 0; i < 16; ++i) {                                                               \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                              \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* global load */                       \
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); /* LDS write */                         \
-    }                                                                                            \
-    for (int i = 0; i < 4; ++i) {                                                                \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* LDS read */                          \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* copy to LDS */                       \
     }                                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    __syncthreads();                                                                             \
-    MX_READ(p, 1 - (st), 0, ((j) + 1) & 3)                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
-    MX_MFMA(q)                                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
-    MX_READ(q, 1 - (st), 1, ((j) + 1) & 3)                                                      \
+    MX_READ(q, STN, 1)                                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                           \
   }
 
-  // Step j uses stage j % 2 and runs as one MX_STEP: at its start, its
-  // operands are being read and register set W holds the blocks of step
-  // j + 1 (loaded during step j - 1).  The barrier sits between the two
-  // halves' products; at it every wavefront has finished reading stage
-  // j % 2's operands for step j (the barrier waits for all LDS accesses)
-  // and has written step j + 1's blocks, so the step after next may
-  // overwrite stage j % 2 and step j + 1's operands may be read, while the
-  // products of half 1 keep the matrix cores busy across it.  Steps past
-  // the last load and read the last step again (in bounds, never used):
-  // unconditional loads keep the register sets out of scratch.  The loop
-  // takes whole pairs of steps; an odd last step follows it.
-  const int last = g.KS - 1;
-  load_x(0);
-  load_y(min(1, last));
-  store_x(0);
-  __syncthreads();
-  MX_READ(p, 0, 0, 0)
-  MX_READ(q, 0, 1, 0)
+  // Step j uses stage j % 4.  Its copy was issued three steps earlier,
+  // right after the barrier at which every wavefront had finished reading
+  // that stage for step j - 4; the barrier before step j's operands are
+  // read follows each wavefront's wait for its own copies of step j.  The
+  // barrier sits between the two halves' products, so the products of half
+  // 1 keep the matrix cores busy while step j + 1's operands are read and
+  // step j + 4's copy is issued.  Steps past the last copy the last step
+  // again (in bounds, never used).  The loop takes groups of four steps
+  // (stages and scale bytes are compile-time in each), a tail of up to three
+  // follows.
+  MX_DMA(g_stage0, 0)
+  MX_DMA(g_stage1, 1)
+  MX_DMA(g_stage2, 2)
+  MX_DMA(g_stage3, 3)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  MX_READ(p, g_stage0, 0)
+  MX_READ(q, g_stage0, 1)
   int j = 0;
-  for (; j + 1 < g.KS; j += 2) {
-    MX_STEP(0, j, x, y)
-    MX_STEP(1, j + 1, y, x)
+  for (; j + 3 < g.KS; j += 4) {
+    MX_STEP(0, j, g_stage0, g_stage1)
+    MX_STEP(1, j + 1, g_stage1, g_stage2)
+    MX_STEP(2, j + 2, g_stage2, g_stage3)
+    MX_STEP(3, j + 3, g_stage3, g_stage0)
   }
-  if (j < g.KS) {  // odd KS: the last step is in stage 0, its operands read
-    MX_MFMA(p)
-    MX_MFMA(q)
-  }
+  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1)
+  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2)
+  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the loop
 #undef MX_STEP
+#undef MX_BARRIER
 #undef MX_MFMA
 #undef MX_ROW
 #undef MX_READ
+#undef MX_LDS4
 #undef MX_LDS16
+#undef MX_DMA
 
   // epilogue: bf16, nearest even; rows >= M and columns >= N are not
-  // stored.  Four neighbouring columns go out as one 8-byte store when the
-  // whole tile lies inside N and C's rows are 8-byte aligned; otherwise one
-  // element at a time.
-  const int row0 = tm * kTileM + 128 * wm + (lane & 31);
-  const int col0 = tn * kTileN + 128 * wn + 4 * (lane >> 5);
-  const bool vec = (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 7) == 0) &&
+  // stored.  When the whole tile lies inside N and C's rows are 16-byte
+  // aligned, each wavefront stages its 128 x 128 block in its own LDS stage
+  // array (rows 272 bytes apart) and writes it back as whole rows, 16 bytes
+  // per lane; otherwise each value goes out on its own.
+  const int row0 = tm * kTileM + 128 * wm;
+  const int col0 = tn * kTileN + 128 * wn;
+  const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
                    (tn + 1) * kTileN <= g.N;
   if (vec) {
+    constexpr int kPitch = 272;  // bytes per staged row
+    uint8_t* stage = wave == 0 ? g_stage0 : wave == 1 ? g_stage1 : wave == 2 ? g_stage2 : g_stage3;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every stage read done
+    __builtin_amdgcn_sched_barrier(0);
+    const int wrow = (lane & 31) * kPitch + 8 * (lane >> 5);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = row0 + 32 * u;
-      if (row >= g.M) continue;
-      uint16_t* crow = g.c + (size_t)row * g.ldc + col0;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = f32_to_bf16_rne(acc[u][v][4 * q]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[u][v][4 * q + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[u][v][4 * q + 2]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[u][v][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(crow + 32 * v + 8 * q) = make_uint2(lo, hi);
+          const f32x2 lo = {acc[u][v][4 * q], acc[u][v][4 * q + 1]};
+          const f32x2 hi = {acc[u][v][4 * q + 2], acc[u][v][4 * q + 3]};
+          const uint2 w = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2)));
+          *reinterpret_cast<uint2*>(stage + wrow + 32 * u * kPitch + 2 * (32 * v + 8 * q)) = w;
         }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wavefront's own rows, lanes exchanged
+    const int rsub = lane >> 4, cchunk = lane & 15;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int r = 4 * i + rsub;
+      const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
+      if (row0 + r < g.M)
+        *reinterpret_cast<uint4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk) = d;
     }
   } else {
+    const int lrow0 = row0 + (lane & 31);
+    const int lcol0 = col0 + 4 * (lane >> 5);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int row = row0 + 32 * u;
+      const int row = lrow0 + 32 * u;
       if (row >= g.M) continue;
       uint16_t* crow = g.c + (size_t)row * g.ldc;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int col = col0 + 32 * v + 8 * (i >> 2) + (i & 3);
+          const int col = lcol0 + 32 * v + 8 * (i >> 2) + (i & 3);
           if (col < g.N) crow[col] = f32_to_bf16_rne(acc[u][v][i]);
         }
     }
@@ -344,20 +342,13 @@ TiledGeom tiled_geometry(int M, int N, int K) {
   t.per_xcd = (int)((tiles + 7) / 8);
   t.grid = 8LL * t.per_xcd;
   t.threads = kTiledThreads;
-  t.lds = kTiledLds;
+  t.lds = 0;  // static: the four stages
   (void)K;
   return t;
 }
 
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
                              int M, int N, int K, hipStream_t stream) {
-  static std::atomic<int> lds_attr_set{0};
-  if (!lds_attr_set.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
-    if (e != hipSuccess) return e;
-    lds_attr_set.store(1, std::memory_order_release);
-  }
   const TiledGeom t = tiled_geometry(M, N, K);
   const PackedDims da = packed_dims(M, K), db = packed_dims(N, K);
   TiledArgs args;
