@@ -143,16 +143,19 @@ void gemm_tiled_kernel(TiledArgs g) {
     ssb_[r] = tb * g.KG * 256;
   }
   const int last = g.KS - 1;
-  // copy step jj (clamped to the last) into stage ST
-#define MX_DMA(ST, jj)                                                                           \
+  // copy step jj (clamped to the last) into stage ST: 8 instructions, 16
+  // when SC (jj % 4 == 0) adds the scale dwords of its group of four steps
+#define MX_DMA(ST, jj, SC)                                                                       \
   {                                                                                              \
     const int js = min((jj), last);                                                              \
     const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                              \
       dma16(ra, ST + kStageA + (wave + 4 * r) * 1024, lane16, sa_[r] + od);                      \
       dma16(rb, ST + kStageB + (wave + 4 * r) * 1024, lane16, sb_[r] + od);                      \
-      dma4(ras, ST + kStageAS + (wave + 4 * r) * 256, lane4, ssa_[r] + os);                      \
-      dma4(rbs, ST + kStageBS + (wave + 4 * r) * 256, lane4, ssb_[r] + os);                      \
+      if (SC) {                                                                                  \
+        dma4(ras, ST + kStageAS + (wave + 4 * r) * 256, lane4, ssa_[r] + os);                    \
+        dma4(rbs, ST + kStageBS + (wave + 4 * r) * 256, lane4, ssb_[r] + os);                    \
+      }                                                                                          \
     }                                                                                            \
   }
 
@@ -171,8 +174,9 @@ void gemm_tiled_kernel(TiledArgs g) {
   // Operands of one half of a K step (64 elements) for the wavefront's
   // 4 x 4 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
   // half 0; half 1 is 512 bytes further for codes and 128 for scales, tile
-  // u (or v) 2048 and 512 further.  The whole scale dword is read; the
-  // instruction picks the step's byte.
+  // u (or v) 2048 and 512 further.  A scale dword holds the bytes of four
+  // steps: it is copied with the group's first step (always into stage 0)
+  // and read once, before that step; the instruction picks each step's byte.
   const int pl0 = (lane & 15) + 16 * (lane >> 5);  // packed lane, K half 0
   const int off_a = kStageA + (8 * wm + half_tile) * 1024 + pl0 * 16;
   const int off_b = kStageB + (8 * wn + half_tile) * 1024 + pl0 * 16;
@@ -183,8 +187,8 @@ void gemm_tiled_kernel(TiledArgs g) {
   int qsa0, qsa1, qsa2, qsa3, qsb0, qsb1, qsb2, qsb3;
 #define MX_LDS16(ST, off) (*reinterpret_cast<const uint4*>(ST + (off)))
 #define MX_LDS4(ST, off) (*reinterpret_cast<const int*>(ST + (off)))
-  // S = p or q, half h, stage ST
-#define MX_READ(S, ST, h)                                                                        \
+  // S = p or q, half h, stage ST; SC: the scale dwords too
+#define MX_READ(S, ST, h, SC)                                                                    \
   {                                                                                              \
     S##a0 = MX_LDS16(ST, off_a + (h) * 512);                                                     \
     S##a1 = MX_LDS16(ST, off_a + (h) * 512 + 2048);                                              \
@@ -194,14 +198,16 @@ void gemm_tiled_kernel(TiledArgs g) {
     S##b1 = MX_LDS16(ST, off_b + (h) * 512 + 2048);                                              \
     S##b2 = MX_LDS16(ST, off_b + (h) * 512 + 4096);                                              \
     S##b3 = MX_LDS16(ST, off_b + (h) * 512 + 6144);                                              \
-    S##sa0 = MX_LDS4(ST, off_as + (h) * 128);                                                    \
-    S##sa1 = MX_LDS4(ST, off_as + (h) * 128 + 512);                                              \
-    S##sa2 = MX_LDS4(ST, off_as + (h) * 128 + 1024);                                             \
-    S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                             \
-    S##sb0 = MX_LDS4(ST, off_bs + (h) * 128);                                                    \
-    S##sb1 = MX_LDS4(ST, off_bs + (h) * 128 + 512);                                              \
-    S##sb2 = MX_LDS4(ST, off_bs + (h) * 128 + 1024);                                             \
-    S##sb3 = MX_LDS4(ST, off_bs + (h) * 128 + 1536);                                             \
+    if (SC) {                                                                                    \
+      S##sa0 = MX_LDS4(ST, off_as + (h) * 128);                                                  \
+      S##sa1 = MX_LDS4(ST, off_as + (h) * 128 + 512);                                            \
+      S##sa2 = MX_LDS4(ST, off_as + (h) * 128 + 1024);                                           \
+      S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                           \
+      S##sb0 = MX_LDS4(ST, off_bs + (h) * 128);                                                  \
+      S##sb1 = MX_LDS4(ST, off_bs + (h) * 128 + 512);                                            \
+      S##sb2 = MX_LDS4(ST, off_bs + (h) * 128 + 1024);                                           \
+      S##sb3 = MX_LDS4(ST, off_bs + (h) * 128 + 1536);                                           \
+    }                                                                                            \
   }
 #define MX_ROW(S, u, k)                                                                          \
   acc[u][0] = mfma32_fp4<k>(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                        \
@@ -210,24 +216,25 @@ void gemm_tiled_kernel(TiledArgs g) {
   acc[u][3] = mfma32_fp4<k>(S##b3, S##a##u, acc[u][3], S##sb3, S##sa##u);
 #define MX_MFMA(S, k) \
   { MX_ROW(S, 0, k) MX_ROW(S, 1, k) MX_ROW(S, 2, k) MX_ROW(S, 3, k) }
-  // Own copies of step j + 1 done (those of steps j + 2 and j + 3, 32
-  // instructions, may be in flight), own LDS accesses done, then the
-  // workgroup barrier.  An asm statement: the compiler's barrier would wait
-  // for every copy in flight.
-#define MX_BARRIER()                                                                             \
+  // Before the barrier that precedes step j + 1's reads: own copies of
+  // step j + 1 done (those of steps j + 2 and j + 3 may be in flight: N
+  // instructions, 16 or 24 by where the groups' scale copies fall), own LDS
+  // accesses done.  An asm statement: the compiler's barrier would wait for
+  // every copy in flight.
+#define MX_BARRIER(N)                                                                            \
   __builtin_amdgcn_sched_barrier(0);                                                             \
-  asm volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");         \
+  asm volatile("s_waitcnt vmcnt(" N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");     \
   __builtin_amdgcn_sched_barrier(0);
   // K step jj = 4i + k, in stage STC; STN is the stage of step jj + 1:
   // products of half 0; barrier; the half-0 operands of step jj + 1 read,
   // the copy of step jj + 4 into STC issued and the products of half 1, all
   // interleaved; the half-1 operands of step jj + 1 read
-#define MX_STEP(k, jj, STC, STN)                                                                 \
+#define MX_STEP(k, jj, STC, STN, N)                                                              \
   {                                                                                              \
     MX_MFMA(p, k)                                                                                \
-    MX_BARRIER()                                                                                 \
-    MX_READ(p, STN, 0)                                                                           \
-    MX_DMA(STC, (jj) + 4)                                                                        \
+    MX_BARRIER(N)                                                                                \
+    MX_READ(p, STN, 0, (k) == 3)                                                                 \
+    MX_DMA(STC, (jj) + 4, (k) == 0)                                                              \
     MX_MFMA(q, k)                                                                                \
     for (int i = 0; i < 16; ++i) {                                                               \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                              \
@@ -235,7 +242,7 @@ void gemm_tiled_kernel(TiledArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* copy to LDS */                       \
     }                                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    MX_READ(q, STN, 1)                                                                           \
+    MX_READ(q, STN, 1, (k) == 3)                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                           \
   }
 
@@ -249,25 +256,25 @@ void gemm_tiled_kernel(TiledArgs g) {
   // again (in bounds, never used).  The loop takes groups of four steps
   // (stages and scale bytes are compile-time in each), a tail of up to three
   // follows.
-  MX_DMA(g_stage0, 0)
-  MX_DMA(g_stage1, 1)
-  MX_DMA(g_stage2, 2)
-  MX_DMA(g_stage3, 3)
+  MX_DMA(g_stage0, 0, true)
+  MX_DMA(g_stage1, 1, false)
+  MX_DMA(g_stage2, 2, false)
+  MX_DMA(g_stage3, 3, false)
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(48)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // step 0 copied
   __builtin_amdgcn_sched_barrier(0);
-  MX_READ(p, g_stage0, 0)
-  MX_READ(q, g_stage0, 1)
+  MX_READ(p, g_stage0, 0, true)
+  MX_READ(q, g_stage0, 1, true)
   int j = 0;
   for (; j + 3 < g.KS; j += 4) {
-    MX_STEP(0, j, g_stage0, g_stage1)
-    MX_STEP(1, j + 1, g_stage1, g_stage2)
-    MX_STEP(2, j + 2, g_stage2, g_stage3)
-    MX_STEP(3, j + 3, g_stage3, g_stage0)
+    MX_STEP(0, j, g_stage0, g_stage1, "16")
+    MX_STEP(1, j + 1, g_stage1, g_stage2, "24")
+    MX_STEP(2, j + 2, g_stage2, g_stage3, "24")
+    MX_STEP(3, j + 3, g_stage3, g_stage0, "16")
   }
-  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1)
-  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2)
-  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3)
+  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, "16")
+  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, "24")
+  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, "24")
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the loop
 #undef MX_STEP
 #undef MX_BARRIER
