@@ -201,14 +201,16 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
 }
 
 // Estimated L2-cold microseconds per call of the tiled mode through
-// mxfp4_gemm, fitted to event timings of six shapes from 256x3072x1536 to
-// 8192^3: the quantizer launch (its A traffic at about 3.2 TB/s), then one
-// round per 256 tiles of 256 x 256, each taking about 1.45 us per 128-K step
-// plus 6 us to start and store; 6 us of launch floor.
+// mxfp4_gemm, fitted to event timings of 13 shapes from 256x3072x1536 to
+// 8192^3 (within 8 % on each): 6.3 us of launch floor, the quantizer launch
+// (its A traffic at about 3.2 TB/s), then one round per 256 tiles of
+// 256 x 256, each taking 5 us plus 0.6 to 0.86 us per 128-K step (the
+// slower when more CUs run at once, as the clock drops).
 double tiled_cost(int M, int N, int K) {
   const double tiles = ceil(M / 256.0) * ceil(N / 256.0);
   const double rounds = ceil(tiles / 256.0);
-  return 6.0 + rounds * (1.45 * ceil(K / 128.0) + 6.0) + 2.65 + (double)M * K * 2.5 / 3.2e6;
+  const double step_us = 0.6 + 0.26 * fmin(1.0, tiles / 256.0);
+  return 6.3 + 2.65 + (double)M * K * 2.5 / 3.2e6 + rounds * (step_us * ceil(K / 128.0) + 5.0);
 }
 
 // plan_cost is relative: it omits the launch floor and, on shapes with
@@ -220,8 +222,8 @@ double absolute_cost(const mxfp4_plan& p, int M, int N, int K) {
 }
 
 // The valid plan (reduce kernel for split-K) of least plan_cost; fused before
-// pre-quantized, so ties keep the single-launch plan.  Shapes with at least
-// 32 tiles of 256 x 256 also weigh the tiled mode.
+// pre-quantized, so ties keep the single-launch plan.  Shapes with M >= 256
+// and at least 16 tiles of 256 x 256 also weigh the tiled mode.
 mxfp4_plan model_plan(int M, int N, int K) {
   static const int ksw_opts[] = {1, 2, 3, 4, 6, 7, 8, 12, 14, 16};
   static const int wk_opts[] = {1, 2, 3, 4, 8};
@@ -251,7 +253,7 @@ mxfp4_plan model_plan(int M, int N, int K) {
           }
         }
     }
-  if (ceil(M / 256.0) * ceil(N / 256.0) >= 32) {
+  if (M >= 256 && ceil(M / 256.0) * ceil(N / 256.0) >= 16) {
     const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, 1, 1, 1, 1);
     if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK &&
         tiled_cost(M, N, K) < absolute_cost(best, M, N, K))

@@ -160,8 +160,8 @@ typedef struct mxfp4_plan {
 
 /* The plan mxfp4_gemm uses for a shape: a per-shape table for the tuned
  * shapes, otherwise the plan of least estimated time under a cost model
- * (fused, pre-quantized or, when M and N give at least 32 tiles of
- * 256 x 256, tiled).  A tiled plan's other fields are 1 and unused.
+ * (fused, pre-quantized or, when M >= 256 and M and N give at least 16
+ * tiles of 256 x 256, tiled).  A tiled plan's other fields are 1 and unused.
  * Errors: ENULL, EINVAL. */
 int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
 

@@ -3,8 +3,9 @@ through the C ABI.
 
 Same bar as the other GEMM parity tests: |C_gpu - C_ref| <= 1e-2*|C_ref| + 1e-2
 elementwise.  Shapes cover one 256 x 256 tile, ragged M and N edges inside a
-tile, K that ends inside a 128-element step, grids whose tile count is not a
-multiple of the 8 XCD slots (some workgroups have no tile), and sampled
+tile, K that ends inside a 128-element step, step counts that leave 0 to 3
+steps after the kernel's last group of four, grids whose tile count is not
+a multiple of the 8 XCD slots (some workgroups have no tile), and sampled
 outputs of large shapes.
 """
 import numpy as np
@@ -31,6 +32,8 @@ TILED = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
     (768, 768, 256),    # 9 tiles: 16 workgroup slots, 7 without a tile
     (513, 1000, 1504),  # N not a multiple of 16, K = 11.75 steps
     (2048, 1040, 2080),
+    (300, 280, 384),    # 3 K steps: only the steps after the last group of four
+    (520, 512, 800),    # 7 K steps, the last partial: one group of four, then 3
 ])
 def test_tiled_full_oracle(M, N, K):
     print("case tiled", M, N, K, flush=True)
@@ -62,13 +65,17 @@ def test_tiled_prequant_entry_and_repeat():
     assert torch.equal(c1.view(torch.int16), c3.view(torch.int16))
 
 
-def test_tiled_strided_output():
+@pytest.mark.parametrize("M,N,K,extra", [
+    (260, 200, 384, 37),  # ldc not a multiple of 8: the value-by-value store
+    (300, 512, 384, 64),  # whole tiles along N, ldc % 8 == 0: rows staged through LDS
+])
+def test_tiled_strided_output(M, N, K, extra):
     """ldc > N: only the M x N block of C is written."""
-    M, N, K = 260, 200, 384
+    print("case tiled ldc", M, N, K, extra, flush=True)
     ref = reference((M, N, K, 5))
     a = to_dev_bf16(ref["a_bits"])
     b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
-    big = torch.full((M + 3, N + 37), 7.0, dtype=torch.bfloat16, device=a.device)
+    big = torch.full((M + 3, N + extra), 7.0, dtype=torch.bfloat16, device=a.device)
     view = big[:M, :N]
     mx.gemm(a, b_packed, N, out=view, plan=TILED)
     torch.cuda.synchronize()
