@@ -12,7 +12,12 @@ median L2-cold event time per call (µs, lower is better).  `ms_per_step`
 is wall time per step including the cache-evicting fills.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-                  [--no-cpu-baseline]
+                  [--large] [--no-cpu-baseline]
+
+--large adds one line per large shape (M >= 1024) run by the tiled
+256 x 256 kernel: the default plan's L2-cold time per call (quantizer launch
+included) and the tiled kernel's time on pre-quantized A, each with its
+fraction of the dense FP4 peak.
 """
 import argparse
 import json
@@ -51,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="m32_k512", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--all", action="store_true", help="one extra JSON line per tuned shape")
+    ap.add_argument("--large", action="store_true",
+                    help="one extra JSON line per large shape (tiled 256 x 256 kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -59,13 +66,18 @@ def parse():
     return ap.parse_args()
 
 
+# large shapes for --large: (M, N, K), seeded like the workloads
+LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
+
+
 class Case:
     """Device-resident inputs and outputs of one shape."""
 
     def __init__(self, name, torch, mx):
-        w = inputs.WORKLOADS[name]
+        w = inputs.WORKLOADS[name] if isinstance(name, str) else name
+        name = w.name
         self.name, self.M, self.N, self.K = name, w.M, w.N, w.K
-        a_bits, b_bits = inputs.make(name)
+        a_bits, b_bits = inputs.make(w)
         dev = torch.device("cuda:0")
         to = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
         self.a = to(a_bits)
@@ -310,6 +322,28 @@ def main():
                               "prepack_us": round(statistics.median(
                                   time_cold(torch, flush, c.pack, 10, 2)), 3)}), flush=True)
             del c
+
+    if args.large:
+        tiled = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
+        for i, (M, N, K) in enumerate(LARGE):
+            w = inputs.Workload("large_m%d_n%d_k%d" % (M, N, K), M, N, K, seed=100 + i)
+            c = Case(w, torch, mx)
+            steps = max(3, min(args.steps, 20))
+            us = time_cold(torch, flush, c.call, steps, 2)
+            ap = mx.quant_a_packed(c.a)
+            pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, plan=tiled)
+            us_pre = time_cold(torch, flush, pre, steps, 2)
+            fl = 2.0 * M * N * K
+            med, med_pre = statistics.median(us), statistics.median(us_pre)
+            print(json.dumps({"shape": w.name, "plan": c.plan.__dict__, "median_us": round(med, 3),
+                              "mfma_frac_fp4": round(fl / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                              "prequant_A_median_us": round(med_pre, 3),
+                              "prequant_A_mfma_frac_fp4": round(
+                                  fl / (med_pre * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                              "hbm_GBps": round(alg_bytes(M, N, K) / (med * 1e-6) / 1e9, 1)}),
+                  flush=True)
+            del c, ap
+            torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

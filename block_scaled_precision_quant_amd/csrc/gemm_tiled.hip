@@ -3,26 +3,27 @@
 // Both operands are MX-packed (16-row tiles, 128-K steps, the 16x16x128
 // instruction's lane order).  A workgroup computes a 256 x 256 tile of C with
 // four wavefronts (2 x 2, 128 x 128 each, one per SIMD so that each can hold
-// its 256 accumulators and the staged loads in registers) using the 32x32x64
-// block-scaled FP4 instruction, which does twice the work per operand byte of
-// the 16x16x128 one.  K advances one 128-element step at a time through a
-// two-stage LDS ring fed from two register sets: a step's global loads are
-// issued two steps before its products and written to LDS after the products
-// of the step before it, so one barrier per step suffices and the loads have
-// two steps' worth of products to arrive.  (Loads straight to LDS would make
-// the compiler wait for the next step's copy before every read of the
-// current one.)  Each wavefront's operands are gathered from the packed
-// blocks with per-lane LDS addresses:
+// its 256 accumulators and two halves' operands in registers) using the
+// 32x32x64 block-scaled FP4 instruction, which does twice the work per
+// operand byte of the 16x16x128 one.  K advances one 128-element step at a
+// time through a four-stage LDS ring (40 KiB per stage, all 160 KiB of the
+// CU) filled by direct global-to-LDS copies, issued three steps ahead of
+// their use with no register staging.  One barrier per step, placed between
+// the products of the step's two K halves, so the matrix cores stay busy
+// across it.  Each wavefront's operands are gathered from the packed blocks
+// with per-lane LDS addresses:
 //
 //   32x32x64 lane L, K half h of the step (elements 64h .. 64h+63):
 //     A row 32u + L%32  ->  16-row tile 2u + (L/16)%2, packed lane
 //     (L%16) + 16*(2h + L/32), i.e. K-group 2h + L/32 of the step;
 //   B column likewise; the scale byte of that (row, K-group) is byte j%4 of
-//   the packed scale dword of the same tile and packed lane.
+//   the packed scale dword of the same tile and packed lane, which the
+//   instruction selects itself.
 //
 //   B is the instruction's first operand, so result register i of lane L
 //   holds row L%32 and column 8*(i/4) + 4*(L/32) + i%4: four neighbouring
-//   columns per register group, stored as one 8-byte write.
+//   columns per register group.  The epilogue rounds them to bf16, stages
+//   each wavefront's 128 x 128 block in LDS and writes it back as whole rows.
 //
 // Rows past M and columns past N read clamped (valid) tiles and are never
 // stored.  Workgroup ids go to the 8 XCDs in turn; each XCD takes a
