@@ -69,6 +69,16 @@ def parse():
 # large shapes for --large: (M, N, K), seeded like the workloads
 LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
 
+# --all also times the alternatives to the default plan where the workload
+# makes a choice: the fastest pre-quantized-A plan of an L2-cold sweep over
+# every valid plan (a separate quantizer launch, then the GEMM), and the
+# tiled mode.  Fields: mode, m_blocks, n_tiles_per_wave, waves_n, waves_k,
+# k_steps_per_wave, split_k.
+ALTERNATIVES = {
+    "m64_n7168_k2048": {"prequant": (2, 2, 1, 4, 2, 8, 1)},
+    "m256_n3072_k1536": {"prequant": (2, 2, 1, 6, 1, 12, 1), "tiled": (3, 1, 1, 1, 1, 1, 1)},
+}
+
 
 class Case:
     """Device-resident inputs and outputs of one shape."""
@@ -313,6 +323,13 @@ def main():
             us = time_cold(torch, flush, c.call, args.steps, args.warmup)
             med = statistics.median(us)
             b = alg_bytes(c.M, c.N, c.K)
+            alt = {}
+            for label, fields in ALTERNATIVES.get(n, {}).items():
+                p = mx.Plan(*fields)
+                ws = mx.new_workspace(mx.workspace_bytes(c.M, c.N, c.K, p), "cuda:0")
+                run = lambda: mx.gemm(c.a, c.b_packed, c.N, out=c.c, workspace=ws, plan=p)
+                alt[label] = {"plan": p.__dict__, "median_us": round(statistics.median(
+                    time_cold(torch, flush, run, args.steps, args.warmup)), 3)}
             print(json.dumps({"shape": n, "plan": c.plan.__dict__, "median_us": round(med, 3),
                               "mean_us": round(statistics.fmean(us), 3),
                               "trimmed_mean_us": round(trimmed_mean(us), 3),
@@ -320,7 +337,8 @@ def main():
                               "mfma_frac_fp4": round(2 * c.M * c.N * c.K / (med * 1e-6) / 1e12
                                                      / FP4_PEAK_TFLOPS, 5),
                               "prepack_us": round(statistics.median(
-                                  time_cold(torch, flush, c.pack, 10, 2)), 3)}), flush=True)
+                                  time_cold(torch, flush, c.pack, 10, 2)), 3),
+                              "alternatives": alt}), flush=True)
             del c
 
     if args.large:
