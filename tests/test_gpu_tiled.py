@@ -83,7 +83,8 @@ def test_tiled_strided_output(M, N, K, extra):
     assert bool((big[:, N:] == 7.0).all()) and bool((big[M:, :] == 7.0).all())
 
 
-@pytest.mark.parametrize("M,N,K", [(1024, 8192, 8192), (4096, 4096, 1024), (8200, 2056, 512)])
+@pytest.mark.parametrize("M,N,K", [(1024, 8192, 8192), (4096, 4096, 1024), (8200, 2056, 512),
+                                   (272, 512, 65536)])  # 512 K steps: long copies offsets
 def test_tiled_large_sampled(M, N, K):
     print("case tiled sampled", M, N, K, flush=True)
     a, b = inputs.make_shape(M, N, K, seed=(M * 13 + N) % 1000)
