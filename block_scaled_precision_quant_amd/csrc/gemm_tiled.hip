@@ -2,9 +2,10 @@
 //
 // Both operands are MX-packed (16-row tiles, 128-K steps, the 16x16x128
 // instruction's lane order).  A workgroup computes a 256 x 256 tile of C with
-// four wavefronts (2 x 2, 128 x 128 each, one per SIMD so that each can hold
-// its 256 accumulators and two halves' operands in registers) using the
-// 32x32x64 block-scaled FP4 instruction, which does twice the work per
+// eight wavefronts (2 x 4, 128 x 64 each, two per SIMD: each holds 128
+// accumulators and two halves' operands in registers, and one wavefront's
+// waits are covered by the other's products) using the 32x32x64
+// block-scaled FP4 instruction, which does twice the work per
 // operand byte of the 16x16x128 one.  K advances one 128-element step at a
 // time through a four-stage LDS ring (40 KiB per stage, all 160 KiB of the
 // CU) filled by direct global-to-LDS copies, issued three steps ahead of
@@ -23,7 +24,7 @@
 //   B is the instruction's first operand, so result register i of lane L
 //   holds row L%32 and column 8*(i/4) + 4*(L/32) + i%4: four neighbouring
 //   columns per register group.  The epilogue rounds them to bf16, stages
-//   each wavefront's 128 x 128 block in LDS and writes it back as whole rows.
+//   each wavefront's 128 x 64 block in LDS and writes it back as whole rows.
 //
 // Rows past M and columns past N read clamped (valid) tiles and are never
 // stored.  Workgroup ids go to the 8 XCDs in turn; each XCD takes a
@@ -36,7 +37,7 @@ namespace mx {
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-constexpr int kTiledThreads = 256;  // 4 wavefronts
+constexpr int kTiledThreads = 512;  // 8 wavefronts
 // LDS bytes of one pipeline stage: A and B data (16 blocks of 1 KiB each),
 // then A and B scale dwords (16 tiles x 64 lanes x 4 B each)
 constexpr int kStageA = 0;
@@ -97,7 +98,7 @@ __device__ inline f32x16 mfma32_fp4(uint4 a, uint4 b, f32x16 acc, int sa, int sb
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 4, 4, kSel, sa, kSel, sb);
 }
 
-__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tiled_kernel(TiledArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,8 +121,8 @@ void gemm_tiled_kernel(TiledArgs g) {
   const PackedDims da = {g.MT, g.KS, g.KG};
   const PackedDims db = {g.NT, g.KS, g.KG};
 
-  // Copies: wavefront w moves blocks w, w + 4, w + 8 and w + 12 of A and of
-  // B (1 KiB each) and the scale dwords of the same tiles (256 B each) of a
+  // Copies: wavefront w moves blocks w and w + 8 of A and of B (1 KiB each)
+  // and the scale dwords of the same tiles (256 B each) of a
   // step into that step's stage; tiles past the operand's last are clamped.
   // They go through buffer descriptors that cover just this workgroup's
   // tiles (offsets from the first tile fit in 32 bits for K <= 2^22), so an
@@ -134,55 +135,55 @@ void gemm_tiled_kernel(TiledArgs g) {
   const BufRsrc ras = make_rsrc(g.ap + a_sc + (size_t)t_a0 * g.KG * 256, a_tiles * g.KG * 256);
   const BufRsrc rbs = make_rsrc(g.bp + b_sc + (size_t)t_b0 * g.KG * 256, b_tiles * g.KG * 256);
   const int lane16 = lane * 16, lane4 = lane * 4;
-  int sa_[4], sb_[4], ssa_[4], ssb_[4];  // wave-uniform offsets of the wavefront's tiles
+  int sa_[2], sb_[2], ssa_[2], ssb_[2];  // wave-uniform offsets of the wavefront's tiles
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ta = min(wave + 4 * r, a_tiles - 1), tb = min(wave + 4 * r, b_tiles - 1);
+  for (int r = 0; r < 2; ++r) {
+    const int ta = min(wave + 8 * r, a_tiles - 1), tb = min(wave + 8 * r, b_tiles - 1);
     sa_[r] = ta * g.KS * kBlockBytes;
     sb_[r] = tb * g.KS * kBlockBytes;
     ssa_[r] = ta * g.KG * 256;
     ssb_[r] = tb * g.KG * 256;
   }
   const int last = g.KS - 1;
-  // copy step jj (clamped to the last) into stage ST: 8 instructions, 16
+  // copy step jj (clamped to the last) into stage ST: 4 instructions, 8
   // when SC (jj % 4 == 0) adds the scale dwords of its group of four steps
 #define MX_DMA(ST, jj, SC)                                                                       \
   {                                                                                              \
     const int js = min((jj), last);                                                              \
     const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
-    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                              \
-      dma16(ra, ST + kStageA + (wave + 4 * r) * 1024, lane16, sa_[r] + od);                      \
-      dma16(rb, ST + kStageB + (wave + 4 * r) * 1024, lane16, sb_[r] + od);                      \
+    _Pragma("unroll") for (int r = 0; r < 2; ++r) {                                              \
+      dma16(ra, ST + kStageA + (wave + 8 * r) * 1024, lane16, sa_[r] + od);                      \
+      dma16(rb, ST + kStageB + (wave + 8 * r) * 1024, lane16, sb_[r] + od);                      \
       if (SC) {                                                                                  \
-        dma4(ras, ST + kStageAS + (wave + 4 * r) * 256, lane4, ssa_[r] + os);                    \
-        dma4(rbs, ST + kStageBS + (wave + 4 * r) * 256, lane4, ssb_[r] + os);                    \
+        dma4(ras, ST + kStageAS + (wave + 8 * r) * 256, lane4, ssa_[r] + os);                    \
+        dma4(rbs, ST + kStageBS + (wave + 8 * r) * 256, lane4, ssb_[r] + os);                    \
       }                                                                                          \
     }                                                                                            \
   }
 
-  const int wm = wave >> 1;  // 0..1: rows 128*wm
-  const int wn = wave & 1;   // 0..1: columns 128*wn
+  const int wm = wave >> 2;  // 0..1: rows 128*wm
+  const int wn = wave & 3;   // 0..3: columns 64*wn
   const int half_tile = (lane >> 4) & 1;
-  // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's 128 x 128; B is
+  // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's 128 x 64; B is
   // the instruction's first operand, so lane L holds row L%32 and columns
   // 8*(i/4) + 4*(L/32) + i%4 (four neighbours per register group)
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[u][v] = f32x16{};
+    for (int v = 0; v < 2; ++v) acc[u][v] = f32x16{};
 
   // Operands of one half of a K step (64 elements) for the wavefront's
-  // 4 x 4 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
+  // 4 x 2 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
   // half 0; half 1 is 512 bytes further for codes and 128 for scales, tile
   // u (or v) 2048 and 512 further.  A scale dword holds the bytes of four
   // steps: it is copied with the group's first step (always into stage 0)
   // and read once, before that step; the instruction picks each step's byte.
   const int pl0 = (lane & 15) + 16 * (lane >> 5);  // packed lane, K half 0
   const int off_a = kStageA + (8 * wm + half_tile) * 1024 + pl0 * 16;
-  const int off_b = kStageB + (8 * wn + half_tile) * 1024 + pl0 * 16;
+  const int off_b = kStageB + (4 * wn + half_tile) * 1024 + pl0 * 16;
   const int off_as = kStageAS + (8 * wm + half_tile) * 256 + pl0 * 4;
-  const int off_bs = kStageBS + (8 * wn + half_tile) * 256 + pl0 * 4;
+  const int off_bs = kStageBS + (4 * wn + half_tile) * 256 + pl0 * 4;
   uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
   int psa0, psa1, psa2, psa3, psb0, psb1, psb2, psb3;
   int qsa0, qsa1, qsa2, qsa3, qsb0, qsb1, qsb2, qsb3;
@@ -197,8 +198,6 @@ void gemm_tiled_kernel(TiledArgs g) {
     S##a3 = MX_LDS16(ST, off_a + (h) * 512 + 6144);                                              \
     S##b0 = MX_LDS16(ST, off_b + (h) * 512);                                                     \
     S##b1 = MX_LDS16(ST, off_b + (h) * 512 + 2048);                                              \
-    S##b2 = MX_LDS16(ST, off_b + (h) * 512 + 4096);                                              \
-    S##b3 = MX_LDS16(ST, off_b + (h) * 512 + 6144);                                              \
     if (SC) {                                                                                    \
       S##sa0 = MX_LDS4(ST, off_as + (h) * 128);                                                  \
       S##sa1 = MX_LDS4(ST, off_as + (h) * 128 + 512);                                            \
@@ -206,20 +205,16 @@ void gemm_tiled_kernel(TiledArgs g) {
       S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                           \
       S##sb0 = MX_LDS4(ST, off_bs + (h) * 128);                                                  \
       S##sb1 = MX_LDS4(ST, off_bs + (h) * 128 + 512);                                            \
-      S##sb2 = MX_LDS4(ST, off_bs + (h) * 128 + 1024);                                           \
-      S##sb3 = MX_LDS4(ST, off_bs + (h) * 128 + 1536);                                           \
     }                                                                                            \
   }
 #define MX_ROW(S, u, k)                                                                          \
   acc[u][0] = mfma32_fp4<k>(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                        \
-  acc[u][1] = mfma32_fp4<k>(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);                        \
-  acc[u][2] = mfma32_fp4<k>(S##b2, S##a##u, acc[u][2], S##sb2, S##sa##u);                        \
-  acc[u][3] = mfma32_fp4<k>(S##b3, S##a##u, acc[u][3], S##sb3, S##sa##u);
+  acc[u][1] = mfma32_fp4<k>(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);
 #define MX_MFMA(S, k) \
   { MX_ROW(S, 0, k) MX_ROW(S, 1, k) MX_ROW(S, 2, k) MX_ROW(S, 3, k) }
   // Before the barrier that precedes step j + 1's reads: own copies of
   // step j + 1 done (those of steps j + 2 and j + 3 may be in flight: N
-  // instructions, 16 or 24 by where the groups' scale copies fall), own LDS
+  // instructions, 8 or 12 by where the groups' scale copies fall), own LDS
   // accesses done.  An asm statement: the compiler's barrier would wait for
   // every copy in flight.
 #define MX_BARRIER(N)                                                                            \
@@ -237,7 +232,7 @@ void gemm_tiled_kernel(TiledArgs g) {
     MX_READ(p, STN, 0, (k) == 3)                                                                 \
     MX_DMA(STC, (jj) + 4, (k) == 0)                                                              \
     MX_MFMA(q, k)                                                                                \
-    for (int i = 0; i < 16; ++i) {                                                               \
+    for (int i = 0; i < 8; ++i) {                                                                \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                              \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* LDS read */                          \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* copy to LDS */                       \
@@ -262,20 +257,20 @@ void gemm_tiled_kernel(TiledArgs g) {
   MX_DMA(g_stage2, 2, false)
   MX_DMA(g_stage3, 3, false)
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // step 0 copied
+  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");  // step 0 copied
   __builtin_amdgcn_sched_barrier(0);
   MX_READ(p, g_stage0, 0, true)
   MX_READ(q, g_stage0, 1, true)
   int j = 0;
   for (; j + 3 < g.KS; j += 4) {
-    MX_STEP(0, j, g_stage0, g_stage1, "16")
-    MX_STEP(1, j + 1, g_stage1, g_stage2, "24")
-    MX_STEP(2, j + 2, g_stage2, g_stage3, "24")
-    MX_STEP(3, j + 3, g_stage3, g_stage0, "16")
+    MX_STEP(0, j, g_stage0, g_stage1, "8")
+    MX_STEP(1, j + 1, g_stage1, g_stage2, "12")
+    MX_STEP(2, j + 2, g_stage2, g_stage3, "12")
+    MX_STEP(3, j + 3, g_stage3, g_stage0, "8")
   }
-  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, "16")
-  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, "24")
-  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, "24")
+  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, "8")
+  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, "12")
+  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, "12")
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the loop
 #undef MX_STEP
 #undef MX_BARRIER
@@ -288,16 +283,17 @@ void gemm_tiled_kernel(TiledArgs g) {
 
   // epilogue: bf16, nearest even; rows >= M and columns >= N are not
   // stored.  When the whole tile lies inside N and C's rows are 16-byte
-  // aligned, each wavefront stages its 128 x 128 block in its own LDS stage
-  // array (rows 272 bytes apart) and writes it back as whole rows, 16 bytes
-  // per lane; otherwise each value goes out on its own.
+  // aligned, each wavefront stages its 128 x 64 block in its own half of an
+  // LDS stage array (rows 144 bytes apart) and writes it back as whole rows,
+  // 16 bytes per lane; otherwise each value goes out on its own.
   const int row0 = tm * kTileM + 128 * wm;
-  const int col0 = tn * kTileN + 128 * wn;
+  const int col0 = tn * kTileN + 64 * wn;
   const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
                    (tn + 1) * kTileN <= g.N;
   if (vec) {
-    constexpr int kPitch = 272;  // bytes per staged row
-    uint8_t* stage = wave == 0 ? g_stage0 : wave == 1 ? g_stage1 : wave == 2 ? g_stage2 : g_stage3;
+    constexpr int kPitch = 144;  // bytes per staged row
+    const int wp = wave >> 1;
+    uint8_t* stage = (wp == 0 ? g_stage0 : wp == 1 ? g_stage1 : wp == 2 ? g_stage2 : g_stage3) + (wave & 1) * 128 * kPitch;
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every stage read done
     __builtin_amdgcn_sched_barrier(0);
@@ -305,7 +301,7 @@ void gemm_tiled_kernel(TiledArgs g) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x2 lo = {acc[u][v][4 * q], acc[u][v][4 * q + 1]};
@@ -315,10 +311,10 @@ void gemm_tiled_kernel(TiledArgs g) {
           *reinterpret_cast<uint2*>(stage + wrow + 32 * u * kPitch + 2 * (32 * v + 8 * q)) = w;
         }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wavefront's own rows, lanes exchanged
-    const int rsub = lane >> 4, cchunk = lane & 15;
+    const int rsub = lane >> 3, cchunk = lane & 7;
 #pragma unroll 8
-    for (int i = 0; i < 32; ++i) {
-      const int r = 4 * i + rsub;
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * i + rsub;
       const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
       if (row0 + r < g.M)
         *reinterpret_cast<uint4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk) = d;
@@ -332,7 +328,7 @@ void gemm_tiled_kernel(TiledArgs g) {
       if (row >= g.M) continue;
       uint16_t* crow = g.c + (size_t)row * g.ldc;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int col = lcol0 + 32 * v + 8 * (i >> 2) + (i & 3);

@@ -127,11 +127,12 @@ def test_tiled_plan(lib):
         assert mx.workspace_bytes(M, N, K, p) == (mx.packed_bytes(M, K) + 255) // 256 * 256
         assert mx.workspace_zero_bytes(M, N, K, p) == 0
         assert mx.prequant_workspace_bytes(M, N, K, p) == 0
-    # 2^20 x 2^20 is 2^24 tiles of 256 threads: one more than a dispatch holds
+    # 2^20 x 2^19 is 2^23 tiles of 512 threads: one work-item more than a
+    # dispatch holds; one tile column fewer fits
     p = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
-    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 20, 128) == EINVAL
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 19, 128) == EINVAL
     assert "grid too large" in mx.load().mxfp4_last_error().decode()
-    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 20) - 256, 128) == 0
+    assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 19) - 256, 128) == 0
     # buffer offsets are 32-bit: K is limited to 2^22
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, 1 << 22) == 0
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, (1 << 22) + 32) == EINVAL
