@@ -130,7 +130,7 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * the GEMM kernel reads fp4 A.
  *
  * mode TILED is the large-M kernel: like PREQUANT it quantizes A into the
- * workspace first, then one workgroup of four wavefronts computes each
+ * workspace first, then one workgroup of eight wavefronts computes each
  * 256 x 256 tile of C over the whole of K with the gfx950 block-scaled
  * 32x32x64 FP4 instruction (the same products and fp32 sums per output as
  * the other modes, in K order; results agree with them within fp32
