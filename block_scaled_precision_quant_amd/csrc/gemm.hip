@@ -37,9 +37,6 @@ struct GemmArgs {
                                 // for every x < 2^32 / kswg (33-bit for kswg = 1)
 };
 
-// LDS-direct loads: each active lane moves 16 (or 4) bytes from its own
-// global address to lds_base + lane*16 (or lane*4); lds_base must be the
-// same for the whole wavefront.
 // 16-byte load marked nontemporal (streamed, not expected to be re-read soon)
 __device__ inline uint4 load_stream16(const void* p) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -47,6 +44,9 @@ __device__ inline uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// LDS-direct loads: each active lane moves 16 (or 4) bytes from its own
+// global address to lds_base + lane*16 (or lane*4); lds_base must be the
+// same for the whole wavefront.
 __device__ inline void lds_load16(const void* gptr, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
