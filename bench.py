@@ -14,10 +14,10 @@ is wall time per step including the cache-evicting fills.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
                   [--large] [--no-cpu-baseline]
 
---large adds one line per large shape (M >= 1024) run by the tiled
-256 x 256 kernel: the default plan's L2-cold time per call (quantizer launch
-included) and the tiled kernel's time on pre-quantized A, each with its
-fraction of the dense FP4 peak.
+--large adds one line per large shape (M >= 1024), whose default plan is the
+tiled kernel: the L2-cold time per call (quantizer launch included) and the
+same plan's time on pre-quantized A, each with its fraction of the dense FP4
+peak.
 """
 import argparse
 import json
@@ -76,7 +76,7 @@ LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
 # k_steps_per_wave, split_k.
 ALTERNATIVES = {
     "m64_n7168_k2048": {"prequant": (2, 2, 1, 4, 2, 8, 1)},
-    "m256_n3072_k1536": {"prequant": (2, 2, 1, 6, 1, 12, 1), "tiled": (3, 1, 1, 1, 1, 1, 1)},
+    "m256_n3072_k1536": {"prequant": (2, 2, 1, 6, 1, 12, 1), "tiled": (3, 1, 1, 2, 1, 1, 1)},
 }
 
 
@@ -342,14 +342,13 @@ def main():
             del c
 
     if args.large:
-        tiled = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
         for i, (M, N, K) in enumerate(LARGE):
             w = inputs.Workload("large_m%d_n%d_k%d" % (M, N, K), M, N, K, seed=100 + i)
             c = Case(w, torch, mx)
             steps = max(3, min(args.steps, 20))
             us = time_cold(torch, flush, c.call, steps, 2)
             ap = mx.quant_a_packed(c.a)
-            pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, plan=tiled)
+            pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, plan=c.plan)
             us_pre = time_cold(torch, flush, pre, steps, 2)
             fl = 2.0 * M * N * K
             med, med_pre = statistics.median(us), statistics.median(us_pre)

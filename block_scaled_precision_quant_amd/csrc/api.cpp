@@ -77,6 +77,10 @@ int check_gemm_shape(int M, int N, int K) {
   return MXFP4_OK;
 }
 
+// Tile width of a tiled plan: waves_n == 2 selects 256 x 128 tiles (four
+// wavefronts), any other value 256 x 256 (eight).
+int tiled_width(const mxfp4_plan& p) { return p.waves_n == 2 ? 128 : 256; }
+
 // Checks a plan against a shape; `mode_matters` is false for the prequant
 // entry point, where the mode only selects the tiled kernel or not.
 int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
@@ -88,10 +92,10 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
                "plan.mode must be MXFP4_MODE_FUSED, MXFP4_MODE_PREQUANT or MXFP4_MODE_TILED (got %d)",
                p.mode);
   if (p.mode == MXFP4_MODE_TILED) {
-    // fixed tiling: the other fields are not used
+    // waves_n picks the tile width; the other fields are not used
     if (K > mx::kTiledMaxK)
       return bad(MXFP4_EINVAL, "MXFP4_MODE_TILED supports K <= %d (got %d)", mx::kTiledMaxK, K);
-    const mx::TiledGeom t = mx::tiled_geometry(M, N, K);
+    const mx::TiledGeom t = mx::tiled_geometry(M, N, K, tiled_width(p));
     if (t.grid * t.threads > 0xFFFFFFFFLL)
       return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", t.grid, t.threads);
     return MXFP4_OK;
@@ -203,13 +207,16 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
 // Estimated L2-cold microseconds per call of the tiled mode through
 // mxfp4_gemm, fitted to event timings of 13 shapes from 256x3072x1536 to
 // 8192^3 (within 8 % on each): 6.3 us of launch floor, the quantizer launch
-// (its A traffic at about 3.2 TB/s), then one round per 256 tiles of
-// 256 x 256, each taking 5 us plus 0.6 to 0.86 us per 128-K step (the
-// slower when more CUs run at once, as the clock drops).
-double tiled_cost(int M, int N, int K) {
-  const double tiles = ceil(M / 256.0) * ceil(N / 256.0);
+// (its A traffic at about 3.2 TB/s), then one round per 256 tiles, each
+// taking 5 us plus, per 128-K step, 0.6 to 0.86 us for a 256 x 256 tile
+// (the slower when more CUs run at once, as the clock drops) and
+// kHalfTileStep of that for a 256 x 128 one.
+constexpr double kHalfTileStep = 0.6;
+double tiled_cost(int M, int N, int K, int width) {
+  const double tiles = ceil(M / 256.0) * ceil(N / (double)width);
   const double rounds = ceil(tiles / 256.0);
-  const double step_us = 0.6 + 0.26 * fmin(1.0, tiles / 256.0);
+  double step_us = 0.6 + 0.26 * fmin(1.0, tiles / 256.0);
+  if (width != 256) step_us *= kHalfTileStep;
   return 6.3 + 2.65 + (double)M * K * 2.5 / 3.2e6 + rounds * (step_us * ceil(K / 128.0) + 5.0);
 }
 
@@ -254,10 +261,17 @@ mxfp4_plan model_plan(int M, int N, int K) {
         }
     }
   if (M >= 256 && ceil(M / 256.0) * ceil(N / 256.0) >= 16) {
-    const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, 1, 1, 1, 1);
-    if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK &&
-        tiled_cost(M, N, K) < absolute_cost(best, M, N, K))
-      return tiled;
+    double best_abs = absolute_cost(best, M, N, K);
+    mxfp4_plan pick = best;
+    for (int wn : {4, 2}) {  // 256 x 256 tiles, then 256 x 128
+      const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, wn, 1, 1, 1);
+      const double t = tiled_cost(M, N, K, tiled_width(tiled));
+      if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK && t < best_abs) {
+        best_abs = t;
+        pick = tiled;
+      }
+    }
+    return pick;
   }
   return best;
 }
@@ -465,7 +479,8 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
   }
   if (p.mode == MXFP4_MODE_TILED) {
     hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_src),
-                                         static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K, st);
+                                         static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
+                                         tiled_width(p), st);
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
     return ok();
   }
@@ -509,7 +524,7 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
   if (p.mode == MXFP4_MODE_TILED) {
     hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_packed),
                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
-                                         static_cast<hipStream_t>(stream));
+                                         tiled_width(p), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
     return ok();
   }

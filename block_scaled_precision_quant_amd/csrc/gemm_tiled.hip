@@ -36,8 +36,8 @@
 namespace mx {
 
 constexpr int kTileM = 256;
-constexpr int kTileN = 256;
-constexpr int kTiledThreads = 512;  // 8 wavefronts
+// Tile width kTN: 256 (eight wavefronts, 2 x 4) or 128 (four, 2 x 2); every
+// wavefront computes 128 rows x 64 columns.
 // LDS bytes of one pipeline stage: A and B data (16 blocks of 1 KiB each),
 // then A and B scale dwords (16 tiles x 64 lanes x 4 B each)
 constexpr int kStageA = 0;
@@ -98,8 +98,28 @@ __device__ inline f32x16 mfma32_fp4(uint4 a, uint4 b, f32x16 acc, int sa, int sb
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 4, 4, kSel, sa, kSel, sb);
 }
 
-__global__ __launch_bounds__(kTiledThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Each wavefront waits for its own copies except the newest N instructions,
+// and for its LDS accesses, then the workgroup barrier.  An asm statement:
+// the compiler's barrier would wait for every copy in flight.
+template <int N>
+__device__ inline void wait_copies_barrier() {
+  static_assert(N == 8 || N == 12 || N == 18, "copy counts of the two tile widths");
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12)
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(18)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int kTN>
+__global__ __launch_bounds__(kTN * 2) __attribute__((amdgpu_waves_per_eu(kTN / 128, kTN / 128)))
 void gemm_tiled_kernel(TiledArgs g) {
+  constexpr int kWaves = kTN / 32;        // 8 or 4
+  constexpr int kWavesN = kWaves / 2;     // wavefronts along N
+  constexpr int kRA = 16 / kWaves;        // A blocks each wavefront copies per step
+  constexpr int kRB = kTN / 16 / kWaves;  // B blocks each wavefront copies per step
+  constexpr int kC = kRA + kRB;           // copy instructions per step (and per scale group)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,7 +136,7 @@ void gemm_tiled_kernel(TiledArgs g) {
   const int tm = first_m + in_group % rows_in;
   const int tn = in_group / rows_in;
   const int t_a0 = tm * (kTileM / 16);  // first 16-row tile of A
-  const int t_b0 = tn * (kTileN / 16);  // first 16-row tile of B
+  const int t_b0 = tn * (kTN / 16);  // first 16-row tile of B
 
   const PackedDims da = {g.MT, g.KS, g.KG};
   const PackedDims db = {g.NT, g.KS, g.KG};
@@ -128,20 +148,24 @@ void gemm_tiled_kernel(TiledArgs g) {
   // tiles (offsets from the first tile fit in 32 bits for K <= 2^22), so an
   // address is one per-lane constant plus a wave-uniform offset.
   const int a_tiles = min(kTileM / 16, g.MT - t_a0);
-  const int b_tiles = min(kTileN / 16, g.NT - t_b0);
+  const int b_tiles = min(kTN / 16, g.NT - t_b0);
   const size_t a_sc = da.data_bytes(), b_sc = db.data_bytes();
   const BufRsrc ra = make_rsrc(g.ap + (size_t)t_a0 * g.KS * kBlockBytes, a_tiles * g.KS * kBlockBytes);
   const BufRsrc rb = make_rsrc(g.bp + (size_t)t_b0 * g.KS * kBlockBytes, b_tiles * g.KS * kBlockBytes);
   const BufRsrc ras = make_rsrc(g.ap + a_sc + (size_t)t_a0 * g.KG * 256, a_tiles * g.KG * 256);
   const BufRsrc rbs = make_rsrc(g.bp + b_sc + (size_t)t_b0 * g.KG * 256, b_tiles * g.KG * 256);
   const int lane16 = lane * 16, lane4 = lane * 4;
-  int sa_[2], sb_[2], ssa_[2], ssb_[2];  // wave-uniform offsets of the wavefront's tiles
+  int sa_[kRA], ssa_[kRA], sb_[kRB], ssb_[kRB];  // wave-uniform offsets of the wavefront's tiles
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int ta = min(wave + 8 * r, a_tiles - 1), tb = min(wave + 8 * r, b_tiles - 1);
+  for (int r = 0; r < kRA; ++r) {
+    const int ta = min(wave + kWaves * r, a_tiles - 1);
     sa_[r] = ta * g.KS * kBlockBytes;
-    sb_[r] = tb * g.KS * kBlockBytes;
     ssa_[r] = ta * g.KG * 256;
+  }
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) {
+    const int tb = min(wave + kWaves * r, b_tiles - 1);
+    sb_[r] = tb * g.KS * kBlockBytes;
     ssb_[r] = tb * g.KG * 256;
   }
   const int last = g.KS - 1;
@@ -151,18 +175,18 @@ void gemm_tiled_kernel(TiledArgs g) {
   {                                                                                              \
     const int js = min((jj), last);                                                              \
     const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
-    _Pragma("unroll") for (int r = 0; r < 2; ++r) {                                              \
-      dma16(ra, ST + kStageA + (wave + 8 * r) * 1024, lane16, sa_[r] + od);                      \
-      dma16(rb, ST + kStageB + (wave + 8 * r) * 1024, lane16, sb_[r] + od);                      \
-      if (SC) {                                                                                  \
-        dma4(ras, ST + kStageAS + (wave + 8 * r) * 256, lane4, ssa_[r] + os);                    \
-        dma4(rbs, ST + kStageBS + (wave + 8 * r) * 256, lane4, ssb_[r] + os);                    \
-      }                                                                                          \
+    _Pragma("unroll") for (int r = 0; r < kRA; ++r) {                                            \
+      dma16(ra, ST + kStageA + (wave + kWaves * r) * 1024, lane16, sa_[r] + od);                 \
+      if (SC) dma4(ras, ST + kStageAS + (wave + kWaves * r) * 256, lane4, ssa_[r] + os);         \
+    }                                                                                            \
+    _Pragma("unroll") for (int r = 0; r < kRB; ++r) {                                            \
+      dma16(rb, ST + kStageB + (wave + kWaves * r) * 1024, lane16, sb_[r] + od);                 \
+      if (SC) dma4(rbs, ST + kStageBS + (wave + kWaves * r) * 256, lane4, ssb_[r] + os);         \
     }                                                                                            \
   }
 
-  const int wm = wave >> 2;  // 0..1: rows 128*wm
-  const int wn = wave & 3;   // 0..3: columns 64*wn
+  const int wm = wave / kWavesN;  // 0..1: rows 128*wm
+  const int wn = wave % kWavesN;  // columns 64*wn
   const int half_tile = (lane >> 4) & 1;
   // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's 128 x 64; B is
   // the instruction's first operand, so lane L holds row L%32 and columns
@@ -214,12 +238,11 @@ void gemm_tiled_kernel(TiledArgs g) {
   { MX_ROW(S, 0, k) MX_ROW(S, 1, k) MX_ROW(S, 2, k) MX_ROW(S, 3, k) }
   // Before the barrier that precedes step j + 1's reads: own copies of
   // step j + 1 done (those of steps j + 2 and j + 3 may be in flight: N
-  // instructions, 8 or 12 by where the groups' scale copies fall), own LDS
-  // accesses done.  An asm statement: the compiler's barrier would wait for
-  // every copy in flight.
+  // instructions, 2 kC or 3 kC by where the groups' scale copies fall), own
+  // LDS accesses done.
 #define MX_BARRIER(N)                                                                            \
   __builtin_amdgcn_sched_barrier(0);                                                             \
-  asm volatile("s_waitcnt vmcnt(" N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");     \
+  wait_copies_barrier<N>();                                                                      \
   __builtin_amdgcn_sched_barrier(0);
   // K step jj = 4i + k, in stage STC; STN is the stage of step jj + 1:
   // products of half 0; barrier; the half-0 operands of step jj + 1 read,
@@ -257,20 +280,20 @@ void gemm_tiled_kernel(TiledArgs g) {
   MX_DMA(g_stage2, 2, false)
   MX_DMA(g_stage3, 3, false)
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");  // step 0 copied
+  wait_copies_barrier<3 * kC>();  // step 0 copied (steps 1-3 may be in flight)
   __builtin_amdgcn_sched_barrier(0);
   MX_READ(p, g_stage0, 0, true)
   MX_READ(q, g_stage0, 1, true)
   int j = 0;
   for (; j + 3 < g.KS; j += 4) {
-    MX_STEP(0, j, g_stage0, g_stage1, "8")
-    MX_STEP(1, j + 1, g_stage1, g_stage2, "12")
-    MX_STEP(2, j + 2, g_stage2, g_stage3, "12")
-    MX_STEP(3, j + 3, g_stage3, g_stage0, "8")
+    MX_STEP(0, j, g_stage0, g_stage1, 2 * kC)
+    MX_STEP(1, j + 1, g_stage1, g_stage2, 3 * kC)
+    MX_STEP(2, j + 2, g_stage2, g_stage3, 3 * kC)
+    MX_STEP(3, j + 3, g_stage3, g_stage0, 2 * kC)
   }
-  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, "8")
-  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, "12")
-  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, "12")
+  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, 2 * kC)
+  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, 3 * kC)
+  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, 3 * kC)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the loop
 #undef MX_STEP
 #undef MX_BARRIER
@@ -287,9 +310,9 @@ void gemm_tiled_kernel(TiledArgs g) {
   // LDS stage array (rows 144 bytes apart) and writes it back as whole rows,
   // 16 bytes per lane; otherwise each value goes out on its own.
   const int row0 = tm * kTileM + 128 * wm;
-  const int col0 = tn * kTileN + 64 * wn;
+  const int col0 = tn * kTN + 64 * wn;
   const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
-                   (tn + 1) * kTileN <= g.N;
+                   (tn + 1) * kTN <= g.N;
   if (vec) {
     constexpr int kPitch = 144;  // bytes per staged row
     const int wp = wave >> 1;
@@ -338,22 +361,22 @@ void gemm_tiled_kernel(TiledArgs g) {
   }
 }
 
-TiledGeom tiled_geometry(int M, int N, int K) {
+TiledGeom tiled_geometry(int M, int N, int K, int tile_n) {
   TiledGeom t;
   t.tiles_m = (int)(((long long)M + kTileM - 1) / kTileM);
-  t.tiles_n = (int)(((long long)N + kTileN - 1) / kTileN);
+  t.tiles_n = (int)(((long long)N + tile_n - 1) / tile_n);
   const long long tiles = (long long)t.tiles_m * t.tiles_n;
   t.per_xcd = (int)((tiles + 7) / 8);
   t.grid = 8LL * t.per_xcd;
-  t.threads = kTiledThreads;
+  t.threads = tile_n * 2;
   t.lds = 0;  // static: the four stages
   (void)K;
   return t;
 }
 
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
-                             int M, int N, int K, hipStream_t stream) {
-  const TiledGeom t = tiled_geometry(M, N, K);
+                             int M, int N, int K, int tile_n, hipStream_t stream) {
+  const TiledGeom t = tiled_geometry(M, N, K, tile_n);
   const PackedDims da = packed_dims(M, K), db = packed_dims(N, K);
   TiledArgs args;
   args.ap = a_packed;
@@ -370,7 +393,9 @@ hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, u
   args.tiles_n = t.tiles_n;
   args.per_xcd = t.per_xcd;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tiled_kernel), dim3((unsigned)t.grid),
+  const void* fn = tile_n == 128 ? reinterpret_cast<const void*>(&gemm_tiled_kernel<128>)
+                                  : reinterpret_cast<const void*>(&gemm_tiled_kernel<256>);
+  return hipLaunchKernel(fn, dim3((unsigned)t.grid),
                          dim3(t.threads), kargs, (unsigned)t.lds, stream);
 }
 

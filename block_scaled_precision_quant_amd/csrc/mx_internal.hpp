@@ -63,8 +63,8 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
                        uint16_t* c, int ldc, int M, int N, int K, float* ws,
                        unsigned* counters, hipStream_t stream);
 
-// Large-M kernel on pre-quantized A (gemm_tiled.hip): 256 x 256 tiles of C,
-// 32x32x64 products, K pipelined through LDS.
+// Large-M kernel on pre-quantized A (gemm_tiled.hip): 256 x tile_n tiles of
+// C (tile_n 256 or 128), 32x32x64 products, K pipelined through LDS.
 // Longest K of the tiled kernel: its buffer offsets within one workgroup's
 // 16 row tiles stay below 2^31.
 constexpr int kTiledMaxK = 1 << 22;
@@ -74,9 +74,9 @@ struct TiledGeom {
   int threads;
   int lds;         // bytes of LDS per workgroup
 };
-TiledGeom tiled_geometry(int M, int N, int K);
+TiledGeom tiled_geometry(int M, int N, int K, int tile_n);
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
-                             int M, int N, int K, hipStream_t stream);
+                             int M, int N, int K, int tile_n, hipStream_t stream);
 
 void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
                          uint8_t* out_scale, int ld_scale, hipStream_t stream);

@@ -130,13 +130,14 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * the GEMM kernel reads fp4 A.
  *
  * mode TILED is the large-M kernel: like PREQUANT it quantizes A into the
- * workspace first, then one workgroup of eight wavefronts computes each
- * 256 x 256 tile of C over the whole of K with the gfx950 block-scaled
- * 32x32x64 FP4 instruction (the same products and fp32 sums per output as
- * the other modes, in K order; results agree with them within fp32
- * rounding, not bit for bit).  Its tiling is fixed: every other plan field
- * is ignored; K must be <= 4194304 (2^22).  It pays off when M and N give
- * many 256 x 256 tiles.
+ * workspace first, then one workgroup computes each tile of C over the
+ * whole of K with the gfx950 block-scaled 32x32x64 FP4 instruction (the
+ * same products and fp32 sums per output as the other modes, in K order;
+ * results agree with them within fp32 rounding, not bit for bit).  Only
+ * waves_n is read: waves_n == 2 selects 256 x 128 tiles (four wavefronts),
+ * any other value 256 x 256 tiles (eight wavefronts); both widths give the
+ * same bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
+ * many tiles.
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1
 #define MXFP4_MODE_PREQUANT 2
@@ -161,7 +162,8 @@ typedef struct mxfp4_plan {
 /* The plan mxfp4_gemm uses for a shape: a per-shape table for the tuned
  * shapes, otherwise the plan of least estimated time under a cost model
  * (fused, pre-quantized or, when M >= 256 and M and N give at least 16
- * tiles of 256 x 256, tiled).  A tiled plan's other fields are 1 and unused.
+ * tiles of 256 x 256, tiled with either tile width).  A tiled plan's
+ * fields other than mode and waves_n are 1 and unused.
  * Errors: ENULL, EINVAL. */
 int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
 

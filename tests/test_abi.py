@@ -128,11 +128,15 @@ def test_tiled_plan(lib):
         assert mx.workspace_zero_bytes(M, N, K, p) == 0
         assert mx.prequant_workspace_bytes(M, N, K, p) == 0
     # 2^20 x 2^19 is 2^23 tiles of 512 threads: one work-item more than a
-    # dispatch holds; one tile column fewer fits
+    # dispatch holds; one tile column fewer fits.  The 256 x 128 tiles
+    # (waves_n == 2) have 256 threads: the same limit in work-items.
     p = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 19, 128) == EINVAL
     assert "grid too large" in mx.load().mxfp4_last_error().decode()
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 19) - 256, 128) == 0
+    p128 = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 1)
+    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, 1 << 19, 128) == EINVAL
+    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, (1 << 19) - 128, 128) == 0
     # buffer offsets are 32-bit: K is limited to 2^22
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, 1 << 22) == 0
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, (1 << 22) + 32) == EINVAL
@@ -247,14 +251,16 @@ def test_default_plans_valid_on_random_shapes(lib):
 
 
 def test_default_plan_mode_by_size(lib):
-    """Small and mid shapes keep the 16x16x128 kernels; shapes with about 64
-    or more 256 x 256 tiles go to the tiled kernel, which measured faster
-    there (1.2x at 1024x4096x4096, 4x at 8192^3)."""
-    for M, N, K in [(4, 2880, 512), (256, 3072, 1536), (512, 7168, 2048), (512, 4096, 4096),
-                    (64, 65536, 4096)]:
+    """Small and mid shapes keep the 16x16x128 kernels; shapes with dozens of
+    256-row tiles or more go to the tiled kernel, which measured faster there
+    (1.2x at 1024x4096x4096, 4x at 8192^3): 256 x 128 tiles while 256 x 256
+    ones would leave CUs idle (1024x8192x8192: 128 of them), 256 x 256 from
+    a full round of those on."""
+    for M, N, K in [(4, 2880, 512), (256, 3072, 1536), (64, 65536, 4096), (1024, 1024, 1024)]:
         assert mx.default_plan(M, N, K).mode != mx.MODE_TILED, (M, N, K)
-    for M, N, K in [(1024, 4096, 4096), (640, 8192, 4096), (1536, 4096, 2048), (1024, 8192, 8192),
-                    (2048, 4096, 4096), (4096, 4096, 4096), (8192, 8192, 8192)]:
+    for M, N, K, wide in [(1024, 4096, 4096, False), (640, 8192, 4096, False), (1536, 4096, 2048, False),
+                          (1024, 8192, 8192, False), (2048, 4096, 4096, False),
+                          (4096, 4096, 4096, True), (8192, 8192, 8192, True)]:
         p = mx.default_plan(M, N, K)
-        assert p.mode == mx.MODE_TILED, (M, N, K, p)
+        assert p.mode == mx.MODE_TILED and (p.waves_n != 2) == wide, (M, N, K, p)
         assert mx.workspace_bytes(M, N, K) == mx.packed_bytes(M, K) + (-mx.packed_bytes(M, K) % 256)

@@ -21,7 +21,9 @@ import block_scaled_precision_quant_amd as mx  # noqa: E402
 from gpu_util import assert_close_to_oracle, bf16_out_to_f32, to_dev_bf16, to_dev_u8  # noqa: E402
 from test_gpu_gemm import reference, run_gemm  # noqa: E402
 
-TILED = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
+TILED = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)      # 256 x 256 tiles
+TILED128 = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 1)   # waves_n == 2: 256 x 128 tiles
+WIDTHS = pytest.mark.parametrize("plan", [TILED, TILED128], ids=["w256", "w128"])
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -35,22 +37,25 @@ TILED = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
     (300, 280, 384),    # 3 K steps: only the steps after the last group of four
     (520, 512, 800),    # 7 K steps, the last partial: one group of four, then 3
 ])
-def test_tiled_full_oracle(M, N, K):
-    print("case tiled", M, N, K, flush=True)
+@WIDTHS
+def test_tiled_full_oracle(M, N, K, plan):
+    print("case tiled", M, N, K, plan.waves_n, flush=True)
     ref = reference((M, N, K, M * 7 + N))
-    assert_close_to_oracle(run_gemm(ref, TILED), ref["c32"], "tiled %dx%dx%d" % (M, N, K))
+    assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "tiled %dx%dx%d %s" % (M, N, K, plan))
 
 
 @pytest.mark.parametrize("name", ["m256_n3072_k1536", "m64_n7168_k2048", "m16_n2112_k7168"])
-def test_tiled_workloads(name):
-    print("case tiled", name, flush=True)
+@WIDTHS
+def test_tiled_workloads(name, plan):
+    print("case tiled", name, plan.waves_n, flush=True)
     ref = reference(name)
-    assert_close_to_oracle(run_gemm(ref, TILED), ref["c32"], "tiled " + name)
+    assert_close_to_oracle(run_gemm(ref, plan), ref["c32"], "tiled %s %s" % (name, plan))
 
 
 def test_tiled_prequant_entry_and_repeat():
     """gemm_prequant with a tiled plan equals the fused-entry tiled call bit
-    for bit (same packed A, same kernel), and a second call repeats it."""
+    for bit (same packed A, same kernel), a second call repeats it, and the
+    256 x 128 tiles give the same bits as the 256 x 256 ones."""
     M, N, K = 520, 300, 1024
     ref = reference((M, N, K, 11))
     a = to_dev_bf16(ref["a_bits"])
@@ -59,25 +64,29 @@ def test_tiled_prequant_entry_and_repeat():
     c1 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=TILED)
     c2 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=TILED)
     c3 = mx.gemm(a, b_packed, N, plan=TILED)
+    c4 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=TILED128)
     torch.cuda.synchronize()
     assert_close_to_oracle(bf16_out_to_f32(c1), ref["c32"], "tiled gemm_prequant")
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
     assert torch.equal(c1.view(torch.int16), c3.view(torch.int16))
+    # both tile widths run the same products per output in the same order
+    assert torch.equal(c1.view(torch.int16), c4.view(torch.int16))
 
 
 @pytest.mark.parametrize("M,N,K,extra", [
     (260, 200, 384, 37),  # ldc not a multiple of 8: the value-by-value store
     (300, 512, 384, 64),  # whole tiles along N, ldc % 8 == 0: rows staged through LDS
 ])
-def test_tiled_strided_output(M, N, K, extra):
+@WIDTHS
+def test_tiled_strided_output(M, N, K, extra, plan):
     """ldc > N: only the M x N block of C is written."""
-    print("case tiled ldc", M, N, K, extra, flush=True)
+    print("case tiled ldc", M, N, K, extra, plan.waves_n, flush=True)
     ref = reference((M, N, K, 5))
     a = to_dev_bf16(ref["a_bits"])
     b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
     big = torch.full((M + 3, N + extra), 7.0, dtype=torch.bfloat16, device=a.device)
     view = big[:M, :N]
-    mx.gemm(a, b_packed, N, out=view, plan=TILED)
+    mx.gemm(a, b_packed, N, out=view, plan=plan)
     torch.cuda.synchronize()
     assert_close_to_oracle(bf16_out_to_f32(view), ref["c32"], "tiled ldc")
     assert bool((big[:, N:] == 7.0).all()) and bool((big[M:, :] == 7.0).all())
@@ -85,15 +94,16 @@ def test_tiled_strided_output(M, N, K, extra):
 
 @pytest.mark.parametrize("M,N,K", [(1024, 8192, 8192), (4096, 4096, 1024), (8200, 2056, 512),
                                    (272, 512, 65536)])  # 512 K steps: long copies offsets
-def test_tiled_large_sampled(M, N, K):
-    print("case tiled sampled", M, N, K, flush=True)
+@WIDTHS
+def test_tiled_large_sampled(M, N, K, plan):
+    print("case tiled sampled", M, N, K, plan.waves_n, flush=True)
     a, b = inputs.make_shape(M, N, K, seed=(M * 13 + N) % 1000)
     aq, asc = oracle.quantize(a)
     bq, bsc = oracle.quantize(b)
     dev_a = to_dev_bf16(a)
     b_packed = mx.pack_b(to_dev_u8(bq), to_dev_u8(bsc))
     c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev_a.device)
-    mx.gemm(dev_a, b_packed, N, out=c, plan=TILED)
+    mx.gemm(dev_a, b_packed, N, out=c, plan=plan)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M + N + K)
     # the first and last rows and columns of tiles, and random ones
