@@ -222,10 +222,11 @@ double tiled_cost(int M, int N, int K, int width) {
 
 // plan_cost is relative: it omits the launch floor and, on shapes with
 // hundreds of thousands of products per CU, the issue rate of the
-// 16x16x128 kernels, which peak at about 0.85 PFLOP/s (measured from M=512
-// up).  Against the tiled mode's absolute estimate they count both.
+// 16x16x128 kernels, which reach 0.6 to 0.85 PFLOP/s there (measured on
+// nine shapes from 512x4096x4096 to 4096^3; 0.7 is used).  Against the
+// tiled mode's absolute estimate they count both.
 double absolute_cost(const mxfp4_plan& p, int M, int N, int K) {
-  return 6.3 + fmax(plan_cost(p, M, N, K), 2.0 * M * N * (double)K / 0.85e9);
+  return 6.3 + fmax(plan_cost(p, M, N, K), 2.0 * M * N * (double)K / 0.7e9);
 }
 
 // The valid plan (reduce kernel for split-K) of least plan_cost; fused before
