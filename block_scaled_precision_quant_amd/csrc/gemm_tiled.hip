@@ -2,9 +2,10 @@
 //
 // Both operands are MX-packed (16-row tiles, 128-K steps, the 16x16x128
 // instruction's lane order).  A workgroup computes a 256 x 256 tile of C with
-// eight wavefronts (2 x 4, 128 x 64 each, two per SIMD: each holds 128
+// eight wavefronts (2 x 4, 128 x 64 each), or a 256 x 128 tile with eight
+// wavefronts of 64 x 64 (4 x 2) -- two per SIMD: each holds its
 // accumulators and two halves' operands in registers, and one wavefront's
-// waits are covered by the other's products) using the 32x32x64
+// waits are covered by the other's products -- using the 32x32x64
 // block-scaled FP4 instruction, which does twice the work per
 // operand byte of the 16x16x128 one.  K advances one 128-element step at a
 // time through a four-stage LDS ring (40 KiB per stage, all 160 KiB of the
@@ -24,7 +25,7 @@
 //   B is the instruction's first operand, so result register i of lane L
 //   holds row L%32 and column 8*(i/4) + 4*(L/32) + i%4: four neighbouring
 //   columns per register group.  The epilogue rounds them to bf16, stages
-//   each wavefront's 128 x 64 block in LDS and writes it back as whole rows.
+//   each wavefront's block in LDS and writes it back as whole rows.
 //
 // Rows past M and columns past N read clamped (valid) tiles and are never
 // stored.  Workgroup ids go to the 8 XCDs in turn; each XCD takes a
@@ -36,8 +37,8 @@
 namespace mx {
 
 constexpr int kTileM = 256;
-// Tile width kTN: 256 (eight wavefronts, 2 x 4) or 128 (four, 2 x 2); every
-// wavefront computes 128 rows x 64 columns.
+// Tiles are 256 rows x kTN columns (kTN 256 or 128); a wavefront computes
+// 32 kU rows x 64 columns (kU 4 or 2), eight wavefronts per workgroup.
 // LDS bytes of one pipeline stage: A and B data (16 blocks of 1 KiB each),
 // then A and B scale dwords (16 tiles x 64 lanes x 4 B each)
 constexpr int kStageA = 0;
@@ -103,8 +104,12 @@ __device__ inline f32x16 mfma32_fp4(uint4 a, uint4 b, f32x16 acc, int sa, int sb
 // the compiler's barrier would wait for every copy in flight.
 template <int N>
 __device__ inline void wait_copies_barrier() {
-  static_assert(N == 8 || N == 12 || N == 18, "copy counts of the two tile widths");
-  if constexpr (N == 8)
+  static_assert(N == 6 || N == 8 || N == 9 || N == 12 || N == 18, "copy counts of the tilings");
+  if constexpr (N == 6)
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 9)
+    asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 12)
     asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -112,11 +117,11 @@ __device__ inline void wait_copies_barrier() {
     asm volatile("s_waitcnt vmcnt(18)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int kTN>
-__global__ __launch_bounds__(kTN * 2) __attribute__((amdgpu_waves_per_eu(kTN / 128, kTN / 128)))
+template <int kTN, int kU>
+__global__ __launch_bounds__(kTN * 8 / kU) __attribute__((amdgpu_waves_per_eu(kTN / (32 * kU), kTN / (32 * kU))))
 void gemm_tiled_kernel(TiledArgs g) {
-  constexpr int kWaves = kTN / 32;        // 8 or 4
-  constexpr int kWavesN = kWaves / 2;     // wavefronts along N
+  constexpr int kWavesN = kTN / 64;       // wavefronts along N (64 columns each)
+  constexpr int kWaves = kWavesN * 8 / kU;  // and 8 / kU along M (32 kU rows each)
   constexpr int kRA = 16 / kWaves;        // A blocks each wavefront copies per step
   constexpr int kRB = kTN / 16 / kWaves;  // B blocks each wavefront copies per step
   constexpr int kC = kRA + kRB;           // copy instructions per step (and per scale group)
@@ -185,28 +190,28 @@ void gemm_tiled_kernel(TiledArgs g) {
     }                                                                                            \
   }
 
-  const int wm = wave / kWavesN;  // 0..1: rows 128*wm
+  const int wm = wave / kWavesN;  // rows 32*kU*wm
   const int wn = wave % kWavesN;  // columns 64*wn
   const int half_tile = (lane >> 4) & 1;
-  // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's 128 x 64; B is
+  // acc[u][v]: rows 32u.., columns 32v.. of the wavefront's block; B is
   // the instruction's first operand, so lane L holds row L%32 and columns
   // 8*(i/4) + 4*(L/32) + i%4 (four neighbours per register group)
-  f32x16 acc[4][2];
+  f32x16 acc[kU][2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < kU; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v) acc[u][v] = f32x16{};
 
   // Operands of one half of a K step (64 elements) for the wavefront's
-  // 4 x 2 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
+  // kU x 2 products: P holds K half 0, Q K half 1.  Per-lane LDS offsets of
   // half 0; half 1 is 512 bytes further for codes and 128 for scales, tile
   // u (or v) 2048 and 512 further.  A scale dword holds the bytes of four
   // steps: it is copied with the group's first step (always into stage 0)
   // and read once, before that step; the instruction picks each step's byte.
   const int pl0 = (lane & 15) + 16 * (lane >> 5);  // packed lane, K half 0
-  const int off_a = kStageA + (8 * wm + half_tile) * 1024 + pl0 * 16;
+  const int off_a = kStageA + (2 * kU * wm + half_tile) * 1024 + pl0 * 16;
   const int off_b = kStageB + (4 * wn + half_tile) * 1024 + pl0 * 16;
-  const int off_as = kStageAS + (8 * wm + half_tile) * 256 + pl0 * 4;
+  const int off_as = kStageAS + (2 * kU * wm + half_tile) * 256 + pl0 * 4;
   const int off_bs = kStageBS + (4 * wn + half_tile) * 256 + pl0 * 4;
   uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
   int psa0, psa1, psa2, psa3, psb0, psb1, psb2, psb3;
@@ -218,15 +223,19 @@ void gemm_tiled_kernel(TiledArgs g) {
   {                                                                                              \
     S##a0 = MX_LDS16(ST, off_a + (h) * 512);                                                     \
     S##a1 = MX_LDS16(ST, off_a + (h) * 512 + 2048);                                              \
-    S##a2 = MX_LDS16(ST, off_a + (h) * 512 + 4096);                                              \
-    S##a3 = MX_LDS16(ST, off_a + (h) * 512 + 6144);                                              \
+    if constexpr (kU == 4) {                                                                     \
+      S##a2 = MX_LDS16(ST, off_a + (h) * 512 + 4096);                                            \
+      S##a3 = MX_LDS16(ST, off_a + (h) * 512 + 6144);                                            \
+    }                                                                                            \
     S##b0 = MX_LDS16(ST, off_b + (h) * 512);                                                     \
     S##b1 = MX_LDS16(ST, off_b + (h) * 512 + 2048);                                              \
     if (SC) {                                                                                    \
       S##sa0 = MX_LDS4(ST, off_as + (h) * 128);                                                  \
       S##sa1 = MX_LDS4(ST, off_as + (h) * 128 + 512);                                            \
-      S##sa2 = MX_LDS4(ST, off_as + (h) * 128 + 1024);                                           \
-      S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                           \
+      if constexpr (kU == 4) {                                                                   \
+        S##sa2 = MX_LDS4(ST, off_as + (h) * 128 + 1024);                                         \
+        S##sa3 = MX_LDS4(ST, off_as + (h) * 128 + 1536);                                         \
+      }                                                                                          \
       S##sb0 = MX_LDS4(ST, off_bs + (h) * 128);                                                  \
       S##sb1 = MX_LDS4(ST, off_bs + (h) * 128 + 512);                                            \
     }                                                                                            \
@@ -234,8 +243,11 @@ void gemm_tiled_kernel(TiledArgs g) {
 #define MX_ROW(S, u, k)                                                                          \
   acc[u][0] = mfma32_fp4<k>(S##b0, S##a##u, acc[u][0], S##sb0, S##sa##u);                        \
   acc[u][1] = mfma32_fp4<k>(S##b1, S##a##u, acc[u][1], S##sb1, S##sa##u);
-#define MX_MFMA(S, k) \
-  { MX_ROW(S, 0, k) MX_ROW(S, 1, k) MX_ROW(S, 2, k) MX_ROW(S, 3, k) }
+#define MX_MFMA(S, k)                                                                            \
+  {                                                                                              \
+    MX_ROW(S, 0, k) MX_ROW(S, 1, k)                                                              \
+    if constexpr (kU == 4) { MX_ROW(S, 2, k) MX_ROW(S, 3, k) }                                   \
+  }
   // Before the barrier that precedes step j + 1's reads: own copies of
   // step j + 1 done (those of steps j + 2 and j + 3 may be in flight: N
   // instructions, 2 kC or 3 kC by where the groups' scale copies fall), own
@@ -255,7 +267,7 @@ void gemm_tiled_kernel(TiledArgs g) {
     MX_READ(p, STN, 0, (k) == 3)                                                                 \
     MX_DMA(STC, (jj) + 4, (k) == 0)                                                              \
     MX_MFMA(q, k)                                                                                \
-    for (int i = 0; i < 8; ++i) {                                                                \
+    for (int i = 0; i < 2 * kU; ++i) {                                                           \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                              \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* LDS read */                          \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* copy to LDS */                       \
@@ -306,23 +318,23 @@ void gemm_tiled_kernel(TiledArgs g) {
 
   // epilogue: bf16, nearest even; rows >= M and columns >= N are not
   // stored.  When the whole tile lies inside N and C's rows are 16-byte
-  // aligned, each wavefront stages its 128 x 64 block in its own half of an
+  // aligned, each wavefront stages its 32 kU x 64 block in its own half of an
   // LDS stage array (rows 144 bytes apart) and writes it back as whole rows,
   // 16 bytes per lane; otherwise each value goes out on its own.
-  const int row0 = tm * kTileM + 128 * wm;
+  const int row0 = tm * kTileM + 32 * kU * wm;
   const int col0 = tn * kTN + 64 * wn;
   const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
                    (tn + 1) * kTN <= g.N;
   if (vec) {
     constexpr int kPitch = 144;  // bytes per staged row
     const int wp = wave >> 1;
-    uint8_t* stage = (wp == 0 ? g_stage0 : wp == 1 ? g_stage1 : wp == 2 ? g_stage2 : g_stage3) + (wave & 1) * 128 * kPitch;
+    uint8_t* stage = (wp == 0 ? g_stage0 : wp == 1 ? g_stage1 : wp == 2 ? g_stage2 : g_stage3) + (wave & 1) * 32 * kU * kPitch;
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every stage read done
     __builtin_amdgcn_sched_barrier(0);
     const int wrow = (lane & 31) * kPitch + 8 * (lane >> 5);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int v = 0; v < 2; ++v)
 #pragma unroll
@@ -336,7 +348,7 @@ void gemm_tiled_kernel(TiledArgs g) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wavefront's own rows, lanes exchanged
     const int rsub = lane >> 3, cchunk = lane & 7;
 #pragma unroll 8
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * kU; ++i) {
       const int r = 8 * i + rsub;
       const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
       if (row0 + r < g.M)
@@ -346,7 +358,7 @@ void gemm_tiled_kernel(TiledArgs g) {
     const int lrow0 = row0 + (lane & 31);
     const int lcol0 = col0 + 4 * (lane >> 5);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int row = lrow0 + 32 * u;
       if (row >= g.M) continue;
       uint16_t* crow = g.c + (size_t)row * g.ldc;
@@ -368,7 +380,7 @@ TiledGeom tiled_geometry(int M, int N, int K, int tile_n) {
   const long long tiles = (long long)t.tiles_m * t.tiles_n;
   t.per_xcd = (int)((tiles + 7) / 8);
   t.grid = 8LL * t.per_xcd;
-  t.threads = tile_n * 2;
+  t.threads = 512;  // eight wavefronts for either width
   t.lds = 0;  // static: the four stages
   (void)K;
   return t;
@@ -393,8 +405,8 @@ hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, u
   args.tiles_n = t.tiles_n;
   args.per_xcd = t.per_xcd;
   void* kargs[] = {&args};
-  const void* fn = tile_n == 128 ? reinterpret_cast<const void*>(&gemm_tiled_kernel<128>)
-                                  : reinterpret_cast<const void*>(&gemm_tiled_kernel<256>);
+  const void* fn = tile_n == 128 ? reinterpret_cast<const void*>(&gemm_tiled_kernel<128, 2>)
+                                  : reinterpret_cast<const void*>(&gemm_tiled_kernel<256, 4>);
   return hipLaunchKernel(fn, dim3((unsigned)t.grid),
                          dim3(t.threads), kargs, (unsigned)t.lds, stream);
 }

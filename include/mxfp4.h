@@ -134,9 +134,9 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * whole of K with the gfx950 block-scaled 32x32x64 FP4 instruction (the
  * same products and fp32 sums per output as the other modes, in K order;
  * results agree with them within fp32 rounding, not bit for bit).  Only
- * waves_n is read: waves_n == 2 selects 256 x 128 tiles (four wavefronts),
- * any other value 256 x 256 tiles (eight wavefronts); both widths give the
- * same bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
+ * waves_n is read: waves_n == 2 selects 256 x 128 tiles, any other value
+ * 256 x 256 tiles (eight wavefronts either way); both widths give the same
+ * bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
  * many tiles.
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1

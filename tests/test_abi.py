@@ -129,14 +129,14 @@ def test_tiled_plan(lib):
         assert mx.prequant_workspace_bytes(M, N, K, p) == 0
     # 2^20 x 2^19 is 2^23 tiles of 512 threads: one work-item more than a
     # dispatch holds; one tile column fewer fits.  The 256 x 128 tiles
-    # (waves_n == 2) have 256 threads: the same limit in work-items.
+    # (waves_n == 2) also have 512 threads: half the columns fit.
     p = mx.Plan(mx.MODE_TILED, 1, 1, 1, 1, 1, 1)
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, 1 << 19, 128) == EINVAL
     assert "grid too large" in mx.load().mxfp4_last_error().decode()
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 1 << 20, (1 << 19) - 256, 128) == 0
     p128 = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 1)
-    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, 1 << 19, 128) == EINVAL
-    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, (1 << 19) - 128, 128) == 0
+    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, 1 << 18, 128) == EINVAL
+    assert lib.mxfp4_check_plan(ctypes.byref(p128._c()), 1 << 20, (1 << 18) - 128, 128) == 0
     # buffer offsets are 32-bit: K is limited to 2^22
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, 1 << 22) == 0
     assert lib.mxfp4_check_plan(ctypes.byref(p._c()), 16, 16, (1 << 22) + 32) == EINVAL
