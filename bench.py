@@ -217,8 +217,9 @@ def cpu_baseline(names, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(N-sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(one GPU's share of an N-sharded GEMM is the same call); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

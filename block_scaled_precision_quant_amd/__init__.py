@@ -189,7 +189,7 @@ def default_plan(M, N, K):
 
 
 def check_plan(plan, M, N, K):
-    """Raise Mxfp4Error unless `plan` is valid for the shape in this build."""
+    """Raise Mxfp4Error unless `plan` is valid for the shape and compiled into the library."""
     cp = plan._c()
     _check(load().mxfp4_check_plan(ctypes.byref(cp), M, N, K))
 

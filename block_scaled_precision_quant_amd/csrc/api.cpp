@@ -114,7 +114,7 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
   const int mode = mode_matters ? p.mode : MXFP4_MODE_PREQUANT;
   if (!mx::gemm_kernel_available(mode, p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave))
     return bad(MXFP4_ENOTSUP,
-                "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this build",
+                "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this library",
                 p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
   const int KS = (int)(((long long)K + 127) / 128);
   if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)

@@ -44,7 +44,7 @@ extern "C" {
 #define MXFP4_ENULL (-2)      /* a required pointer is NULL */
 #define MXFP4_EWORKSPACE (-3) /* workspace smaller than the plan needs */
 #define MXFP4_ESIZE (-4)      /* a packed buffer is smaller than its layout */
-#define MXFP4_ENOTSUP (-5)    /* plan fields not available in this build */
+#define MXFP4_ENOTSUP (-5)    /* plan fields with no compiled kernel */
 #define MXFP4_EHIP (-6)       /* the HIP runtime reported a launch error */
 
 /* ------------------------------------------------------------------------
@@ -167,7 +167,7 @@ typedef struct mxfp4_plan {
  * Errors: ENULL, EINVAL. */
 int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
 
-/* MXFP4_OK when `plan` is valid for the shape and compiled in this build;
+/* MXFP4_OK when `plan` is valid for the shape and has a compiled kernel;
  * otherwise the status mxfp4_gemm_ex would return for it (EINVAL, ENOTSUP,
  * ENULL), with the reason in mxfp4_last_error(). */
 int mxfp4_check_plan(const mxfp4_plan *plan, int M, int N, int K);
