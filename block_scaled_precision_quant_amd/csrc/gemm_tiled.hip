@@ -320,7 +320,9 @@ void gemm_tiled_kernel(TiledArgs g) {
   // stored.  When the whole tile lies inside N and C's rows are 16-byte
   // aligned, each wavefront stages its 32 kU x 64 block in its own half of an
   // LDS stage array (rows 144 bytes apart) and writes it back as whole rows,
-  // 16 bytes per lane; otherwise each value goes out on its own.
+  // 16 bytes per lane, nontemporal (C is not read again: at 8192^3 the call
+  // takes about 3 % less time after the cache eviction than with plain
+  // stores); otherwise each value goes out on its own.
   const int row0 = tm * kTileM + 32 * kU * wm;
   const int col0 = tn * kTN + 64 * wn;
   const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
@@ -352,7 +354,8 @@ void gemm_tiled_kernel(TiledArgs g) {
       const int r = 8 * i + rsub;
       const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
       if (row0 + r < g.M)
-        *reinterpret_cast<uint4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk) = d;
+        __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w},
+                                    reinterpret_cast<u32x4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk));
     }
   } else {
     const int lrow0 = row0 + (lane & 31);

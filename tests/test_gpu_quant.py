@@ -87,6 +87,10 @@ def test_quant_a_special_groups():
     q2, s2 = mx.quant_a(t)
     torch.cuda.synchronize()
     assert np.array_equal(q2.cpu().numpy(), rq) and np.array_equal(s2.cpu().numpy(), rs)
+    # the same groups through the packed quantizer
+    buf = mx.quant_a_packed(t)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), pack_host(rq, rs))
 
 
 @pytest.mark.parametrize("M,K", [(1, 128), (4, 512), (17, 640), (64, 2048), (16, 7168),
@@ -100,6 +104,19 @@ def test_quant_a_packed_layout(M, K):
     assert np.array_equal(got, pack_host(rq, rs))
     q, s = unpack_host(got, M, K)
     assert np.array_equal(q, rq) and np.array_equal(s, rs)
+
+
+@pytest.mark.parametrize("M,K,lda", [(300, 2080, 2088), (33, 1056, 1064), (16, 512, 1024)])
+def test_quant_a_packed_strided(M, K, lda):
+    """Rows lda elements apart (a column slice of a wider matrix); ragged row
+    tile, K ending inside a 128-K step and a group of four steps."""
+    a, _ = inputs.make_shape(M, 16, K, seed=M + lda)
+    rq, rs = oracle.quantize(a)
+    wide = np.zeros((M, lda), dtype=a.dtype)
+    wide[:, :K] = a
+    buf = mx.quant_a_packed(to_dev_bf16(wide)[:, :K])
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), pack_host(rq, rs))
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (2880, 512), (2112, 7168), (48, 640),
