@@ -92,6 +92,42 @@ def test_tiled_strided_output(M, N, K, extra, plan):
     assert bool((big[:, N:] == 7.0).all()) and bool((big[M:, :] == 7.0).all())
 
 
+@WIDTHS
+def test_tiled_max_k_sampled(plan):
+    """K at the tiled mode's limit (2^22, 32768 K steps: the largest offsets
+    the per-workgroup buffer descriptors carry), ragged M and N.  Elements
+    are integers in [-2, 2] (drawn on the GPU from a seeded generator): they
+    quantize exactly, every product is an integer of magnitude <= 4 and every
+    partial sum an integer of magnitude <= 2^24, so the fp32 sums of the
+    oracle and of the kernel are exact in any order and the usual tolerance
+    measures the kernel alone.  B is prepared by the packed quantizer
+    (bit-exact to the oracle's quantization in test_gpu_quant); the oracle
+    quantizes the sampled bf16 rows of A and B itself."""
+    M, N, K = 272, 136, 1 << 22
+    print("case tiled max K", M, N, K, plan.waves_n, flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(4194304)
+    a = torch.randint(-2, 3, (M, K), generator=gen, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b = torch.randint(-2, 3, (N, K), generator=gen, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b_packed = mx.quant_a_packed(b)
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mx.gemm(a, b_packed, N, out=c, plan=plan)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 271])
+    cols = np.array([0, 15, 127, 128, 135])
+
+    def host_bits(t, idx):
+        return t[torch.as_tensor(idx, device=t.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+
+    aq, asc = oracle.quantize(host_bits(a, rows))
+    bq, bsc = oracle.quantize(host_bits(b, cols))
+    want, want64 = oracle.gemm(oracle.dequantize(aq, asc), oracle.dequantize(bq, bsc))
+    assert np.array_equal(want.astype(np.float64), want64)  # the sums are exact
+    r = torch.as_tensor(rows, device=c.device)
+    q = torch.as_tensor(cols, device=c.device)
+    assert_close_to_oracle(bf16_out_to_f32(c[r][:, q]), want, "tiled max K")
+    assert not torch.isnan(c).any().item()
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 8192, 8192), (4096, 4096, 1024), (8200, 2056, 512),
                                    (272, 512, 65536)])  # 512 K steps: long copies offsets
 @WIDTHS
