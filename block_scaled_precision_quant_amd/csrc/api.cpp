@@ -205,19 +205,20 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
 }
 
 // Estimated L2-cold microseconds per call of the tiled mode through
-// mxfp4_gemm, fitted to event timings of 13 shapes from 256x3072x1536 to
-// 8192^3 (within 8 % on each): 6.3 us of launch floor, the quantizer launch
-// (its A traffic at about 3.2 TB/s), then one round per 256 tiles, each
-// taking 5 us plus, per 128-K step, 0.6 to 0.86 us for a 256 x 256 tile
-// (the slower when more CUs run at once, as the clock drops) and
-// kHalfTileStep of that for a 256 x 128 one.
-constexpr double kHalfTileStep = 0.6;
+// mxfp4_gemm, fitted to event timings of 39 runs (18 shapes from
+// 256x4096x4096 to 3072x3072x1024 at both tile widths, and 1024x8192x8192,
+// 4096^3 and 8192^3; within 10 % on all but one, 14 %): the launch floor,
+// the quantizer's launch and its A traffic at 5.7 TB/s (its measured rate),
+// then per round of up to 256 tiles 0.55 us plus, per 128-K step, 0.61 to
+// 1.03 us for a 256 x 256 tile (the slower when more CUs run at once, as the
+// clock drops) and kHalfTileStep of that for a 256 x 128 one.
+constexpr double kHalfTileStep = 0.608;
 double tiled_cost(int M, int N, int K, int width) {
   const double tiles = ceil(M / 256.0) * ceil(N / (double)width);
   const double rounds = ceil(tiles / 256.0);
-  double step_us = 0.6 + 0.26 * fmin(1.0, tiles / 256.0);
+  double step_us = 0.613 + 0.413 * fmin(1.0, tiles / 256.0);
   if (width != 256) step_us *= kHalfTileStep;
-  return 6.3 + 2.65 + (double)M * K * 2.5 / 3.2e6 + rounds * (step_us * ceil(K / 128.0) + 5.0);
+  return 10.48 + (double)M * K * 2.5 / 5.7e6 + rounds * (step_us * ceil(K / 128.0) + 0.55);
 }
 
 // plan_cost is relative: it omits the launch floor and, on shapes with
