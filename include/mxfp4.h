@@ -27,7 +27,11 @@
  *   - return value 0 is success; a negative value is one of MXFP4_E* below.
  *     On any error other than MXFP4_EHIP nothing has been enqueued.  The
  *     text of the last error of the calling thread is mxfp4_last_error();
- *   - calls are thread-safe; the library holds no per-call device state.
+ *   - calls are thread-safe; the library holds no per-call device state;
+ *   - a call enqueues kernel launches only (no allocation, memset or
+ *     synchronization), so it can be captured into a HIP graph; a replay
+ *     reads the buffers as they are at replay time, and replays that share
+ *     a workspace must not overlap, like calls.
  */
 #ifndef MXFP4_H
 #define MXFP4_H
