@@ -205,10 +205,12 @@ def cpu_baseline(names, seconds):
         return time.perf_counter() - t0, sum(counts)
 
     dt1, n1 = run(1, seconds / 2)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))
     dtn, nn = run(cores, max(1.0, seconds * 1.5 / cores))
     return {"value": dtn / nn * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
             "single_thread_value": dt1 / n1 * 1e6,
+            "host_cpu_count": os.cpu_count(), "host_affinity": affinity,
             "sample": "full oracle calls over the workload's shapes (%s): %d calls on %d threads "
                       "in %.1f s wall; single thread: %d calls in %.1f s"
                       % (", ".join(names), nn, cores, dtn, n1, dt1)}
