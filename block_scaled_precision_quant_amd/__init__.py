@@ -17,14 +17,14 @@ from dataclasses import dataclass
 __all__ = [
     "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "MODE_TILED", "REDUCE_KERNEL", "REDUCE_LAST_WG",
     "REDUCE_ATOMIC", "library_path", "load", "packed_bytes",
-    "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes", "gemm",
-    "gemm_prequant", "version",
+    "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes",
+    "prequant_workspace_bytes", "new_workspace", "gemm", "gemm_prequant", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 MODE_FUSED = 1
 MODE_PREQUANT = 2
-MODE_TILED = 3  # 256 x 256 tiles, 32x32x64 instruction; other plan fields ignored
+MODE_TILED = 3  # 32x32x64 instruction; waves_n == 2: 256 x 128 tiles, else 256 x 256; other fields ignored
 REDUCE_KERNEL = 0
 REDUCE_LAST_WG = 1
 REDUCE_ATOMIC = 2
