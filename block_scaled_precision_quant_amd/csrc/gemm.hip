@@ -544,7 +544,11 @@ struct KernelEntry {
 
 static const KernelEntry kKernels[] = {MX_ALL_KERNELS(MX_ENTRY)};
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
-static std::atomic<int> g_lds_attr_set[kNumKernels];
+// Kernels whose LDS exceeds 64 KiB need the dynamic-LDS limit raised once per
+// device (the attribute belongs to the function on the current device);
+// devices past kAttrDevices raise it on every such launch.
+constexpr int kAttrDevices = 64;
+static std::atomic<int> g_lds_attr_set[kAttrDevices][kNumKernels];
 
 static int find_kernel(int mode, int mbw, int ntw, int ksw) {
   for (int i = 0; i < kNumKernels; ++i)
@@ -587,10 +591,16 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   if (ki < 0) return hipErrorInvalidDeviceFunction;
   const GemmGeom geo = gemm_geometry(p, M, N, K);
   const void* fn = kKernels[ki].fn;
-  if (geo.lds_total > 64 * 1024 && !g_lds_attr_set[ki].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  if (geo.lds_total > 64 * 1024) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    g_lds_attr_set[ki].store(1, std::memory_order_release);
+    const bool cached = dev >= 0 && dev < kAttrDevices;
+    if (!cached || !g_lds_attr_set[dev][ki].load(std::memory_order_acquire)) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+      if (e != hipSuccess) return e;
+      if (cached) g_lds_attr_set[dev][ki].store(1, std::memory_order_release);
+    }
   }
   GemmArgs args;
   args.a = p.mode == 1 ? static_cast<const uint16_t*>(a) : nullptr;

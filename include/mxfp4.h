@@ -20,8 +20,9 @@
  * Conventions for every call below:
  *   - pointers named a, b_*, c, workspace, *_packed and out_* are DEVICE
  *     pointers; the plan pointer is a HOST pointer;
- *   - `stream` is a hipStream_t (NULL = the default stream); all device work
- *     is enqueued asynchronously on it and nothing is synchronised;
+ *   - `stream` is a hipStream_t (NULL = the default stream) of the current
+ *     device, whose memory the device pointers must be; all device work is
+ *     enqueued asynchronously on it and nothing is synchronised;
  *   - the library never allocates or frees device memory: the caller owns
  *     every buffer, and the size queries say how large each must be;
  *   - return value 0 is success; a negative value is one of MXFP4_E* below.
