@@ -191,6 +191,27 @@ def test_group_scale_invariance():
         assert np.array_equal(st.astype(int), s0.astype(int) + t)
 
 
+def test_requantization_keeps_values():
+    """Quantizing the dequantized values again gives the same values (an
+    encoding's fixed-point property): every value of a group is a code value
+    times the group's scale, the new group maximum is one of them, and the
+    scale rule then picks the same or a smaller scale under which all of them
+    are exact codes, at any scale.  Groups drawn over 160 binades, one
+    saturating group (significand 1.625) included."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((64, 512)) * np.exp2(rng.integers(-80, 80, (64, 1)))
+    x[0, :32] = 1.625 * np.exp2(rng.integers(-20, 20, 32))  # saturating maxima
+    a = inputs.f32_to_bf16_bits(x.astype(np.float32).reshape(-1)).reshape(x.shape)
+    q1, s1 = oracle.quantize(a)
+    d1 = oracle.dequantize(q1, s1)
+    assert np.all(s1 >= 2)  # dequantized values are normal bf16 numbers
+    a2 = inputs.f32_to_bf16_bits(d1.astype(np.float32).reshape(-1)).reshape(d1.shape)
+    assert np.array_equal(inputs.bf16_bits_to_f32(a2).astype(np.float64), d1)  # exact in bf16
+    q2, s2 = oracle.quantize(a2)
+    assert np.array_equal(oracle.dequantize(q2, s2), d1)
+    assert np.all(s2.astype(int) <= s1.astype(int))
+
+
 # --------------------------------------------------------------- dequantize
 
 
