@@ -260,6 +260,8 @@ def test_default_plan_mode_by_size(lib):
         assert mx.default_plan(M, N, K).mode != mx.MODE_TILED, (M, N, K)
     for M, N, K, wide in [(1024, 4096, 4096, False), (640, 8192, 4096, False), (1536, 4096, 2048, False),
                           (1024, 8192, 8192, False), (2048, 4096, 4096, False),
+                          # measured 17.9 vs 19.7 and 26.5 vs 33.3 us against the best other plans
+                          (384, 6144, 2048, False), (2048, 1024, 4096, False),
                           (4096, 4096, 4096, True), (8192, 8192, 8192, True)]:
         p = mx.default_plan(M, N, K)
         assert p.mode == mx.MODE_TILED and (p.waves_n != 2) == wide, (M, N, K, p)
