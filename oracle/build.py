@@ -13,15 +13,16 @@ SRC = os.path.join(HERE, "mxfp4_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(force: bool = True, out: str = LIB, mutant: int = 0) -> str:
-    """Compile the oracle; returns the library path.  `mutant` > 0 plants one
-    known mistake (for the test that checks the pins catch it)."""
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+def build(force: bool = True, out: str = LIB, src: str = SRC, extra_flags=()) -> str:
+    """Compile the oracle; returns the library path.  `src` may name a
+    modified copy of the source (the pin-strength test plants known mistakes
+    in such copies); `extra_flags` are added to the gcc line (the sanitizer
+    build)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
         return out
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-DORACLE_MUTANT=%d" % mutant,
-           "-o", tmp, SRC, "-lm"]
+           "-ffp-contract=off", "-Wall", "-Wextra"] + list(extra_flags) + ["-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

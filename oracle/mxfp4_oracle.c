@@ -24,12 +24,6 @@
 
 #define ORACLE_GROUP 32
 
-/* ORACLE_MUTANT plants one known mistake (1..9) for the test that checks
- * the pins catch it; the normal build leaves it undefined (0). */
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-
 /* The eight magnitudes an e2m1 code can take, indexed by the low three bits
  * of the code.  Submission 694791 (page 4), `_mxfp4_quant_tile`: the largest
  * magnitude is 6 = 1.5 * 2^2; codes below 1.0 are the subnormal 0 and 0.5. */
@@ -60,9 +54,9 @@ static float bf16_value(uint16_t h) {
  * exponent -127, which the clamp already gives. */
 int oracle_scale_byte(float amax) {
     uint32_t u = f32_bits(amax);
-    u = (u + (ORACLE_MUTANT == 1 ? 0x00400000u : 0x00200000u)) & 0xFF800000u;
+    u = (u + 0x00200000u) & 0xFF800000u;
     int biased = (int)((u >> 23) & 0xFFu);
-    int s = biased - 127 - (ORACLE_MUTANT == 2 ? 1 : 2);
+    int s = biased - 127 - 2;
     if (s < -127) s = -127;
     if (s > 127) s = 127;
     return s + 127;
@@ -81,19 +75,19 @@ int oracle_e2m1_code(float x, int scale_byte) {
     double mag = fabs(q);
     int code;
     if (mag >= 6.0) {
-        code = ORACLE_MUTANT == 3 ? 6 : 7;
+        code = 7;
     } else {
         code = 0;
         double best = mag; /* distance to E2M1_MAGNITUDE[0] == 0 */
         for (int c = 1; c < 8; ++c) {
             double d = fabs(mag - E2M1_MAGNITUDE[c]);
-            if (d < best || (d == best && (c % 2) == (ORACLE_MUTANT == 4 ? 1 : 0))) {
+            if (d < best || (d == best && (c % 2) == 0)) {
                 best = d;
                 code = c;
             }
         }
     }
-    if (ORACLE_MUTANT == 5 ? (x < 0) : signbit(x)) code |= 8;
+    if (signbit(x)) code |= 8;
     return code;
 }
 
@@ -109,7 +103,7 @@ int oracle_e2m1_codes(const float *x, const int32_t *scale_bytes, int64_t n, uin
  * page 3, pads its scale buffer with 127 for that reason). */
 double oracle_dequant_value(int code, int scale_byte) {
     double v = ldexp(E2M1_MAGNITUDE[code & 7], scale_byte - 127);
-    return ((code & 8) && ORACLE_MUTANT != 9) ? -v : v;
+    return (code & 8) ? -v : v;
 }
 
 /* Quantize `rows` rows of K bf16 values (row stride `ld` elements) into
@@ -138,7 +132,7 @@ int oracle_quantize_rows(const uint16_t *x, int64_t rows, int64_t K, int64_t ld,
                 int lo = oracle_e2m1_code(bf16_value(grp[i]), byte);
                 int hi = oracle_e2m1_code(bf16_value(grp[i + 1]), byte);
                 fp4[r * (K / 2) + g * (ORACLE_GROUP / 2) + i / 2] =
-                    (uint8_t)(ORACLE_MUTANT == 6 ? (hi | (lo << 4)) : (lo | (hi << 4)));
+                    (uint8_t)(lo | (hi << 4));
             }
         }
     }
@@ -176,8 +170,8 @@ int oracle_gemm(const double *a_deq, const double *b_deq, int64_t M, int64_t N, 
             const double *b = b_deq + n * K;
             float s32 = 0.0f;
             double s64 = 0.0;
-            for (int64_t k = 0; k < (ORACLE_MUTANT == 8 ? K - 1 : K); ++k) {
-                double p = a[k] * (ORACLE_MUTANT == 7 ? b_deq[k * N + n] : b[k]);
+            for (int64_t k = 0; k < K; ++k) {
+                double p = a[k] * b[k];
                 s32 += (float)p;
                 s64 += p;
             }

@@ -266,6 +266,28 @@ def test_gemm_all_ones_is_row_sum():
     np.testing.assert_array_equal(ref["c64"], np.tile(bd.sum(axis=1), (M, 1)))
 
 
+def test_gemm_abs_closed_forms():
+    """The absolute-product sum used by the error bounds: with every product
+    non-negative (A and B of one sign) it is the exact sum itself, so it
+    equals the fp64 sum bit for bit (same terms, same order); with all-ones
+    A it is the row sum of |deqB|; flipping the sign of either operand
+    leaves it unchanged; and it bounds |C| from above (triangle inequality)."""
+    M, N, K = 5, 16, 256
+    a, b = inputs.make_shape(M, N, K, seed=24)
+    pos = oracle.reference(a & np.uint16(0x7FFF), b & np.uint16(0x7FFF), want64=True)
+    np.testing.assert_array_equal(oracle.gemm_abs(pos["ad"], pos["bd"]), pos["c64"])
+    ref = oracle.reference(a, b, want64=True)
+    ad, bd = ref["ad"], ref["bd"]
+    cabs = oracle.gemm_abs(ad, bd)
+    np.testing.assert_array_equal(oracle.gemm_abs(-ad, bd), cabs)
+    np.testing.assert_array_equal(oracle.gemm_abs(ad, -bd), cabs)
+    assert np.all(cabs >= np.abs(ref["c64"]))
+    ones = np.ones((2, K))
+    np.testing.assert_array_equal(oracle.gemm_abs(ones, bd),
+                                  np.tile(np.abs(decode_with_table(ref["bq"], ref["bs"])).sum(axis=1),
+                                          (2, 1)))
+
+
 def test_gemm_b_scale_shift():
     """Scaling B by 2^t scales C by exactly 2^t."""
     M, N, K = 4, 16, 256
