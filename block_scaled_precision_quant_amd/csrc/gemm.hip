@@ -360,25 +360,30 @@ __global__ __launch_bounds__(kMaxThreads) void gemm_kernel(GemmArgs g) {
 
   // ---- 6. split-K finished by the last workgroup of this output tile.
   //         The partials above are agent-scope atomic stores (or, for the
-  //         atomic reduce, agent-scope atomic adds into one accumulator),
-  //         which are coherent across the XCDs' L2 caches without an L2
-  //         write-back; once they have completed (waitcnt) the tile counter
-  //         is bumped, and the workgroup that takes it to split-1 reads them
-  //         with agent-scope atomic loads.  Last-workgroup reduce: the
-  //         partials are summed in order s = 0..split-1 (the order of
+  //         atomic reduce, agent-scope atomic adds into one accumulator).
+  //         Ordering, in the HIP memory model: the barrier orders every
+  //         thread's partial stores before thread 0's increment of the tile
+  //         counter, an acquire-release read-modify-write at agent scope (on
+  //         gfx950: an L2 write-back before it, an invalidate after it).  The
+  //         workgroup whose increment takes the counter to split-1 has
+  //         therefore acquired every other workgroup's release, and its
+  //         second barrier passes that on to all of its threads, which then
+  //         read the partials.  Last-workgroup reduce: the partials are
+  //         summed in order s = 0..split-1 (the order of
   //         splitk_reduce_kernel, so both give identical bits).  Atomic
   //         reduce: the accumulator already holds the sum (its order of
   //         additions varies from call to call) and is cleared again.  The
-  //         counter returns to zero for the next call on this workspace.  The
-  //         flag lives in the first LDS word: every LDS read above is behind
-  //         the first barrier here.
+  //         counter returns to zero for the next call on this workspace (a
+  //         later launch, ordered by the kernel boundary).  The flag lives in
+  //         the first LDS word: every LDS read above is behind the first
+  //         barrier here.
   volatile int* is_last = reinterpret_cast<volatile int*>(smem);
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_waitcnt(0);  // every wavefront's stores have completed at the barrier
   __syncthreads();
   const int tile = mg * g.ngroups + ng;
   if (tid == 0) {
     const unsigned old =
-        __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     *is_last = (old == (unsigned)(g.split - 1));
   }
   __syncthreads();

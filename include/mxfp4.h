@@ -76,6 +76,12 @@ extern "C" {
 size_t mxfp4_packed_bytes(int rows, int K);
 
 /* One-time repack of a quantized B into the MX-packed layout.
+ * The pages receive B already quantized and pre-shuffled for the matrix
+ * instruction and never time that step (submission 752099, the harness's
+ * `B_shuffle` / `B_scale_sh` operands); submission 739530 `fgemm_pq` shows
+ * what the instruction needs per lane: 16 bytes of codes of one row's
+ * 32-element K-group and that group's scale byte.  This call is that
+ * one-time step for this library's own layout.
  *   b_fp4   [N][K/2]  fp4x2, row-major, contiguous (16-byte aligned);
  *   b_scale [N][K/32] e8m0,  row-major, contiguous;
  *   b_packed  output, mxfp4_packed_bytes(N, K) bytes, 16-byte aligned.
@@ -97,7 +103,10 @@ int mxfp4_quant_a(const uint16_t *a, int M, int K, int lda, uint8_t *out_fp4, in
                   uint8_t *out_scale, int ld_scale, void *stream);
 
 /* Quantize bf16 rows straight into the MX-packed layout (the layout the
- * GEMM reads), padding rows included.
+ * GEMM reads), padding rows included.  The separate pre-quantization of A
+ * of submission 739530 (`prequant`: codes and scales written once, then
+ * read by the GEMM), with the scale and element rules of mxfp4_quant_a,
+ * written in the GEMM's operand layout instead of a linear one.
  *   a  as for mxfp4_quant_a;  out_packed  mxfp4_packed_bytes(M, K) bytes,
  *   16-byte aligned.  Requires M >= 1, K >= 32, K % 32 == 0.  Applied to a
  *   weight matrix B [N][K] this is the one-time B preparation straight from
@@ -198,7 +207,13 @@ size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan *plan, int M, int N, int
 /* Workspace bytes of the default plan (same layout and zero-fill rule). */
 size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
 
-/* C = A . B^T with the default plan.
+/* C = A . B^T with the default plan: the block-scaled product of
+ * submission 752099 `_quant_gemm_fused_launcher` (A quantized in the
+ * kernel, `tl.dot_scaled` of two e2m1 operands with their e8m0 scales,
+ * fp32 accumulation, bf16 result) and submission 739530 `fgemm_pq` (the
+ * gfx950 scaled FP4 matrix instruction; rows past M take scale 0 and are
+ * not stored).  C[m][n] = sum over k of deqA[m][k] * deqB[n][k], summed in
+ * fp32 in an order that depends on the plan, rounded to bf16 (nearest even).
  *   a         [M][lda] bf16, 16-byte aligned, lda % 8 == 0, lda >= K;
  *   b_packed  MX-packed B of N rows (from mxfp4_pack_b), b_packed_bytes >=
  *             mxfp4_packed_bytes(N, K);
@@ -213,7 +228,12 @@ int mxfp4_gemm(const uint16_t *a, int lda, const void *b_packed, size_t b_packed
                uint16_t *c, int ldc, int M, int N, int K, void *workspace,
                size_t workspace_bytes, void *stream);
 
-/* As mxfp4_gemm with an explicit plan (NULL = default plan). */
+/* As mxfp4_gemm with an explicit plan (NULL = default plan).  The plan
+ * chooses among the pages' schemes: A quantized inside the GEMM (submission
+ * 752099 `_quant_gemm_fused_launcher`) or by a separate pre-quantization
+ * launch (submission 739530 `prequant` + `fgemm_pq`), and K split over
+ * workgroups with fp32 partials summed by a second kernel (submission 752099
+ * `_splitk_sum_launcher`, submission 739530 `_reduce_k`). */
 int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
                   uint16_t *c, int ldc, int M, int N, int K, void *workspace,
                   size_t workspace_bytes, const mxfp4_plan *plan, void *stream);
@@ -224,7 +244,9 @@ size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N,
 
 /* GEMM on an A that is already MX-packed (from mxfp4_quant_a_packed), for
  * callers that quantize one activation once and use it against several
- * weights.  Plan mode MXFP4_MODE_TILED runs the tiled kernel (no workspace);
+ * weights: the GEMM half of submission 739530's two-kernel path
+ * (`fgemm_pq`, A read as fp4 codes and scale bytes).  Plan mode
+ * MXFP4_MODE_TILED runs the tiled kernel (no workspace);
  * any other mode value means the plan's tiling with fp4 A, as in PREQUANT
  * mode.  NULL plan = the default plan.  Workspace: as for mxfp4_gemm_ex with
  * the plan in PREQUANT mode, minus the MX-packed A part (tile counters, then
