@@ -1,23 +1,32 @@
-"""Benchmark: L2-cold microseconds per MXFP4 GEMM call on one MI355X.
+"""Benchmark: L2-cold microseconds per MXFP4 GEMM call on one MI355X, for each
+of the six benchmark shapes of the amd-mxfp4-mm pages.
 
-Default workload: the two M=32, K=512 shapes (N=4096 and N=2880).  One step
-is one call of each shape; before every timed call a 512 MiB device fill
-evicts the L2 caches and the Infinity Cache, and HIP events on the launch
-stream bracket the call alone.  Inputs (A bf16, packed B) are resident in
-HBM before timing starts; B is quantized by the library's own quantizer and
-repacked once (reported separately as prepack_us).
+One step is one call of every shape (4x2880x512, 32x4096x512, 32x2880x512,
+16x2112x7168, 64x7168x2048, 256x3072x1536).  Before every timed call a
+512 MiB device fill evicts the L2 caches and the Infinity Cache, and HIP
+events on the launch stream bracket the call alone (launch and scheduling
+included).  The kernels' own durations come from rocprofv3 traces of this
+same command, recorded under profiles/ with the kernel sources' sha256 and
+used only while the sources still match.
+Inputs (A bf16, packed B) are resident in HBM before timing starts; B is
+quantized by the library's quantizer and repacked once (timed separately,
+prepack_us).
 
-Prints one JSON line.  `value` is the mean over the workload's shapes of the
-median L2-cold event time per call (µs, lower is better).  `ms_per_step`
-is wall time per step including the cache-evicting fills.
+Prints one JSON line.  `value` is the median L2-cold event time per call of
+the largest shape by bytes, 64x7168x2048 (us, lower is better); every shape's
+figures are under config.shapes.  `roofline` is that shape's GEMM kernel
+against the HBM peak: algorithmic bytes over the kernel's traced duration
+(`frac`), and over the live event time per call (`frac_event`); `fp4_mfma`
+is the compute-leaning 256x3072x1536 shape against the dense FP4 peak.
+`ms_per_step` is wall time per step, cache-evicting fills included.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
-                  [--large] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--alternatives] [--large]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--copy-calibration]
 
+--alternatives adds one line per shape that has a choice, timing the other
+plans (A pre-quantized by a separate launch, the tiled kernel) the same way.
 --large adds one line per large shape (M >= 1024), whose default plan is the
-tiled kernel: the L2-cold time per call (quantizer launch included) and the
-same plan's time on pre-quantized A, each with its fraction of the dense FP4
-peak.
+tiled kernel.
 """
 import argparse
 import json
@@ -36,12 +45,19 @@ from block_scaled_precision_quant_amd import inputs  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0
 FLUSH_BYTES = 512 << 20
+VALUE_SHAPE = "m64_n7168_k2048"    # the largest shape by bytes: headline value and HBM roofline
+MFMA_SHAPE = "m256_n3072_k1536"    # the compute-leaning shape: FP4 matrix-core fraction
 
-WORKLOAD_SETS = {
-    "m32_k512": ["m32_n4096_k512", "m32_n2880_k512"],
+# The pages' own figures for this path, quoted as context only (another
+# harness on the same GPU model; not a target): submission 705642's notes on
+# the library baseline at M=4.
+PAGES_CONTEXT = {
+    "library_baseline_us_m4": 8.2,
+    "memory_floor_us_m4": 0.13,
+    "source": "kernelindex.com kernelbot-amd-mxfp4-mm-705642, v3 docstring (anatomy of the "
+              "library baseline at M=4): about 8.2 us per call against a memory floor of "
+              "about 0.13 us; context only",
 }
-for _n in inputs.ORDER:
-    WORKLOAD_SETS[_n] = [_n]
 
 
 def alg_bytes(M, N, K):
@@ -49,31 +65,32 @@ def alg_bytes(M, N, K):
     return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="m32_k512", choices=sorted(WORKLOAD_SETS))
-    ap.add_argument("--all", action="store_true", help="one extra JSON line per tuned shape")
+    ap.add_argument("--alternatives", action="store_true",
+                    help="one extra JSON line per shape with a plan choice")
     ap.add_argument("--large", action="store_true",
-                    help="one extra JSON line per large shape (tiled 256 x 256 kernel)")
+                    help="one extra JSON line per large shape (tiled kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="wall seconds of the all-cores oracle run (plus one single-thread "
+                         "call per shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 64 MiB device copy first (a known-size kernel for "
                          "scaling hardware byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # large shapes for --large: (M, N, K), seeded like the workloads
 LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
 
-# --all also times the alternatives to the default plan where the workload
-# makes a choice: the fastest pre-quantized-A plan of an L2-cold sweep over
-# every valid plan (a separate quantizer launch, then the GEMM), and the
-# tiled mode.  Fields: mode, m_blocks, n_tiles_per_wave, waves_n, waves_k,
-# k_steps_per_wave, split_k.
+# --alternatives: the other plans where a shape makes a choice -- the fastest
+# pre-quantized-A plan of an L2-cold sweep over every valid plan (a separate
+# quantizer launch, then the GEMM) and the tiled mode.  Fields: mode,
+# m_blocks, n_tiles_per_wave, waves_n, waves_k, k_steps_per_wave, split_k.
 ALTERNATIVES = {
     "m64_n7168_k2048": {"prequant": (2, 2, 1, 4, 2, 8, 1)},
     "m256_n3072_k1536": {"prequant": (2, 2, 1, 6, 1, 12, 1), "tiled": (3, 1, 1, 2, 1, 1, 1)},
@@ -83,10 +100,9 @@ ALTERNATIVES = {
 class Case:
     """Device-resident inputs and outputs of one shape."""
 
-    def __init__(self, name, torch, mx):
+    def __init__(self, name, torch, mx, plan=None):
         w = inputs.WORKLOADS[name] if isinstance(name, str) else name
-        name = w.name
-        self.name, self.M, self.N, self.K = name, w.M, w.N, w.K
+        self.name, self.M, self.N, self.K = w.name, w.M, w.N, w.K
         a_bits, b_bits = inputs.make(w)
         dev = torch.device("cuda:0")
         to = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -95,8 +111,8 @@ class Case:
         self.bq, self.bs = mx.quant_a(b)  # the library's quantizer on B's rows
         self.b_packed = torch.empty(mx.packed_bytes(self.N, self.K), dtype=torch.uint8, device=dev)
         self.c = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
-        self.plan = mx.default_plan(self.M, self.N, self.K)
-        nws = mx.workspace_bytes(self.M, self.N, self.K)
+        self.plan = plan or mx.default_plan(self.M, self.N, self.K)
+        nws = mx.workspace_bytes(self.M, self.N, self.K, self.plan)
         self.ws = mx.new_workspace(nws, dev) if nws else None  # zeroed tile counters
         self.mx = mx
         mx.pack_b(self.bq, self.bs, out=self.b_packed)
@@ -108,9 +124,39 @@ class Case:
     def call(self):
         self.mx.gemm(self.a, self.b_packed, self.N, out=self.c, workspace=self.ws, plan=self.plan)
 
+    def launches(self):
+        p = self.plan
+        return 1 + (p.mode in (2, 3)) + (p.mode in (1, 2) and p.split_k > 1 and p.split_reduce == 0)
 
-def time_cold(torch, flush, fn, steps, warmup):
-    """Median/mean µs of fn() with an L2 + Infinity Cache eviction before each call."""
+
+def time_cold(torch, flush, cases, steps, warmup):
+    """Per case: event microseconds of `steps` calls, each after a
+    cache-evicting fill.  Returns ({name: [us]}, wall seconds of the timed
+    steps)."""
+    for _ in range(warmup):
+        for c in cases:
+            flush.zero_()
+            c.call()
+    torch.cuda.synchronize()
+    evs = {c.name: [] for c in cases}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for c in cases:
+            flush.zero_()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c.call()
+            e1.record()
+            evs[c.name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {n: [a.elapsed_time(b) * 1e3 for a, b in v] for n, v in evs.items()}, wall
+
+
+def time_cold_fn(torch, flush, fn, steps, warmup):
+    """Event microseconds of fn() after a cache-evicting fill (for calls that
+    are not workload calls: the pre-pack, the 1-byte fill)."""
     for _ in range(warmup):
         flush.zero_()
         fn()
@@ -125,8 +171,7 @@ def time_cold(torch, flush, fn, steps, warmup):
         e1.record()
         evs.append((e0, e1))
     torch.cuda.synchronize()
-    us = [a.elapsed_time(b) * 1000.0 for a, b in evs]
-    return us
+    return [a.elapsed_time(b) * 1000.0 for a, b in evs]
 
 
 def trimmed_mean(us):
@@ -136,7 +181,7 @@ def trimmed_mean(us):
 
 
 def kernel_sources_sha():
-    """sha256 over the HIP sources; hardware byte counters recorded under
+    """sha256 over the HIP sources; hardware counters recorded under
     profiles/ are only reported while the kernels are unchanged."""
     import hashlib
     h = hashlib.sha256()
@@ -147,37 +192,65 @@ def kernel_sources_sha():
     return h.hexdigest()
 
 
-def recorded_profile(workload):
-    """The committed rocprofv3 record for the workload (HBM bytes per launch
-    from the FETCH_SIZE/WRITE_SIZE runs, median traced kernel duration), or
-    None when the kernel sources have changed since it was taken."""
+def recorded_profiles():
+    """The committed rocprofv3 record of this command (profiles/traffic.json:
+    per shape the traced kernel durations, HBM bytes per call from the
+    FETCH_SIZE/WRITE_SIZE runs and, for the compute-leaning shape, matrix-core
+    counters; the empty-kernel durations of the same trace), only while the
+    kernel sources hash to the sha it was taken with; {} otherwise."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    entry = rec.get(workload)
-    if not entry or entry.get("kernel_sources_sha") != kernel_sources_sha():
-        return None
-    return entry
+        return {}
+    if rec.get("kernel_sources_sha") != kernel_sources_sha():
+        return {}
+    return rec
 
 
-def cpu_baseline(names, seconds):
+def shape_label(c):
+    return "M=%d N=%d K=%d" % (c.M, c.N, c.K)
+
+
+def summarize(c, ev, prof):
+    b, fl = alg_bytes(c.M, c.N, c.K), 2 * c.M * c.N * c.K
+    med = statistics.median(ev)
+    out = {
+        "median_us": round(med, 3), "trimmed_mean_us": round(trimmed_mean(ev), 3),
+        "mean_us": round(statistics.fmean(ev), 3), "min_us": round(min(ev), 3),
+        "launches": c.launches(), "plan": c.plan.__dict__, "alg_bytes": b, "flops": fl,
+        "hbm_frac_event": round(b / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "mfma_frac_event": round(fl / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 5),
+    }
+    p = prof.get(c.name)
+    if p:
+        k = p["kernel_us"]  # sum of the call's kernels' median traced durations
+        out["kernel_us"] = k
+        out["kernels"] = p.get("kernels")
+        out["hbm_frac_kernel"] = round(b / (k * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        out["mfma_frac_kernel"] = round(fl / (k * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 5)
+        if p.get("hbm_bytes_per_call"):
+            out["hbm_bytes_counted"] = p["hbm_bytes_per_call"]
+            out["hbm_bytes_over_alg"] = round(p["hbm_bytes_per_call"] / b, 3)
+    return out
+
+
+def cpu_baseline(names, main_name, seconds):
     """The oracle as it stands, on the same inputs: quantize A, dequantize A
     and B, fp32 dot.  B's quantization is excluded, as it is in the GPU call
-    (B arrives pre-quantized).  Timed on one thread, then on every host core
-    the process may use (at most 16): one thread per core, each running
-    whole oracle calls (the oracle's C routines release the interpreter
-    lock).  About 2*seconds of CPU work in all."""
+    (B arrives pre-quantized).  One call of every shape on one thread, then
+    whole calls of the main shape on every host core the process may use (at
+    most 16, one thread each; the oracle's C routines release the
+    interpreter lock) for about `seconds` of wall time."""
     import threading
 
     import oracle
-    prepared = []
+    prepared = {}
     for n in names:
         a, b = inputs.make(n)
         bq, bs = oracle.quantize(b)
-        prepared.append((a, bq, bs))
+        prepared[n] = (a, bq, bs)
 
     def one_call(a, bq, bs):
         aq, asc = oracle.quantize(a)
@@ -185,39 +258,42 @@ def cpu_baseline(names, seconds):
         bd = oracle.dequantize(bq, bs)
         oracle.gemm(ad, bd, want64=False)
 
-    def run(threads, wall_s):
-        counts = [0] * threads
-        stop = time.perf_counter() + wall_s
-
-        def worker(i):
-            while True:
-                for x in prepared:
-                    one_call(*x)
-                    counts[i] += 1
-                if time.perf_counter() >= stop:
-                    return
+    single = {}
+    for n in names:
         t0 = time.perf_counter()
-        ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
-        for t in ts:
-            t.start()
-        for t in ts:
-            t.join()
-        return time.perf_counter() - t0, sum(counts)
+        one_call(*prepared[n])
+        single[n] = round((time.perf_counter() - t0) * 1e6, 1)
 
-    dt1, n1 = run(1, seconds / 2)
     affinity = len(os.sched_getaffinity(0))
     cores = max(1, min(16, affinity))
-    dtn, nn = run(cores, max(1.0, seconds * 1.5 / cores))
-    return {"value": dtn / nn * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
-            "single_thread_value": dt1 / n1 * 1e6,
+    counts = [0] * cores
+    stop = time.perf_counter() + seconds
+
+    def worker(i):
+        while True:
+            one_call(*prepared[main_name])
+            counts[i] += 1
+            if time.perf_counter() >= stop:
+                return
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(cores)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    wall = time.perf_counter() - t0
+    calls = sum(counts)
+    return {"value": round(wall / calls * 1e6, 1), "unit": "us/call", "cores": cores,
+            "kind": "oracle", "shape": main_name,
+            "single_thread_us_per_call": single,
             "host_cpu_count": os.cpu_count(), "host_affinity": affinity,
-            "sample": "full oracle calls over the workload's shapes (%s): %d calls on %d threads "
-                      "in %.1f s wall; single thread: %d calls in %.1f s"
-                      % (", ".join(names), nn, cores, dtn, n1, dt1)}
+            "sample": "%d whole oracle calls of %s on %d threads in %.1f s wall (value = wall / "
+                      "calls); one call of each shape on one thread (single_thread_us_per_call)"
+                      % (calls, main_name, cores, wall)}
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(one GPU's share of an N-sharded GEMM is the same call); run with --gpus 1",
@@ -227,8 +303,7 @@ def main():
 
     import block_scaled_precision_quant_amd as mx
 
-    names = WORKLOAD_SETS[args.workload]
-    cases = [Case(n, torch, mx) for n in names]
+    cases = [Case(n, torch, mx) for n in inputs.ORDER]
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda:0")
@@ -237,58 +312,40 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # timed region: K steps, each one cold call per shape
-    for _ in range(args.warmup):
-        for c in cases:
-            flush.zero_()
-            c.call()
-    torch.cuda.synchronize()
-    ev = {c.name: [] for c in cases}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for c in cases:
-            flush.zero_()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            c.call()
-            e1.record()
-            ev[c.name].append((e0, e1))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {}
+    ev, wall = time_cold(torch, flush, cases, args.steps, args.warmup)
+    rec = recorded_profiles()
+    prof = rec.get("shapes", {})
+    per = {c.name: summarize(c, ev[c.name], prof) for c in cases}
     for c in cases:
-        us = [a.elapsed_time(b) * 1000.0 for a, b in ev[c.name]]
-        per[c.name] = {"median_us": statistics.median(us), "mean_us": statistics.fmean(us),
-                       "trimmed_mean_us": trimmed_mean(us), "min_us": min(us),
-                       "plan": c.plan.__dict__,
-                       "alg_bytes": alg_bytes(c.M, c.N, c.K), "flops": 2 * c.M * c.N * c.K}
-    value = statistics.fmean(p["median_us"] for p in per.values())
+        per[c.name]["prepack_us"] = round(statistics.median(
+            time_cold_fn(torch, flush, c.pack, 10, 2)), 3)
 
     # the same protocol around the smallest kernel there is (a 1-element
-    # fill): the event-timing floor of one launch after the cache eviction
+    # fill): the event-time floor of one launch after the cache eviction
     tiny = torch.zeros(1, dtype=torch.uint8, device="cuda:0")
-    floor_us = statistics.median(time_cold(torch, flush, tiny.zero_, 20, 3))
+    floor = time_cold_fn(torch, flush, tiny.zero_, 20, 3)
 
-    # dominant kernel: the GEMM kernel; with single-launch plans the event pair
-    # brackets exactly that kernel, so achieved = algorithmic bytes per launch
-    # over the mean event duration per launch in the timed region
-    tot_bytes = sum(p["alg_bytes"] for p in per.values())
-    tot_us = sum(p["median_us"] for p in per.values())
-    mean_us = statistics.fmean(p["mean_us"] for p in per.values())
-    achieved = tot_bytes / len(per) / (mean_us * 1e-6) / 1e9
-    tot_flops = sum(p["flops"] for p in per.values())
-    prof = recorded_profile(args.workload)
-    for c in cases:
-        p = per[c.name]
-        p["hbm_GBps"] = p["alg_bytes"] / (p["median_us"] * 1e-6) / 1e9
-        p["hbm_frac"] = p["hbm_GBps"] / HBM_PEAK_GBPS
-        p["mfma_frac"] = p["flops"] / (p["median_us"] * 1e-6) / 1e12 / FP4_PEAK_TFLOPS
-        p["prepack_us"] = statistics.median(time_cold(torch, flush, c.pack, 10, 2))
+    main_case = next(c for c in cases if c.name == VALUE_SHAPE)
+    mfma_case = next(c for c in cases if c.name == MFMA_SHAPE)
+    vb = alg_bytes(main_case.M, main_case.N, main_case.K)
+    e_mean = statistics.fmean(ev[VALUE_SHAPE])
+    mp = prof.get(VALUE_SHAPE, {})
+    main_kernel = (mp.get("kernels") or [{}])[0]
+    if main_kernel.get("mean_us"):
+        # the GEMM kernel's average traced duration in this same command
+        k_mean = main_kernel["mean_us"]
+        basis = "rocprofv3 kernel trace of this command (profiles/), average duration"
+    else:
+        k_mean = e_mean
+        basis = "event time per call (no kernel trace recorded for these kernel sources)"
+    achieved = vb / (k_mean * 1e-6) / 1e9
+    mfl = 2 * mfma_case.M * mfma_case.N * mfma_case.K
+    mprof = prof.get(MFMA_SHAPE, {})
+    m_us = mprof.get("kernel_us")
 
     line = {
         "metric": "L2-cold us/call per (M,N,K) + achieved HBM TB/s and FP4 MFMA % of peak",
-        "value": round(value, 3),
+        "value": per[VALUE_SHAPE]["median_us"],
         "unit": "us/call",
         "n_gpus": 1,
         "steps": args.steps,
@@ -299,68 +356,66 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4(e2m1)+e8m0 x fp4 -> fp32 acc, bf16 in/out",
         "data": "synthetic (seeded normal A and B, bf16)",
-        "config": {"workload": "mxfp4_gemm " + " + ".join(
-            "M=%d N=%d K=%d" % (c.M, c.N, c.K) for c in cases), "shapes": per},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": prof and prof.get("bytes_per_launch"),
-                     "kernel": "gemm_kernel (one launch per call)",
-                     "launch_us_mean": round(mean_us, 3),
-                     # the same kernel's rocprofv3 duration (committed trace of this
-                     # command): the event pair also brackets dispatch overhead
-                     "kernel_us_rocprof": prof and prof.get("kernel_ns_median") and
-                     round(prof["kernel_ns_median"] / 1000.0, 3),
-                     "achieved_at_kernel_us": prof and prof.get("kernel_ns_median") and
-                     round(tot_bytes / len(per) / (prof["kernel_ns_median"] * 1e-9) / 1e9, 1)},
-        "event_floor_us": round(floor_us, 3),
-        "hbm_TBps": round(achieved / 1000.0, 4),
-        "mfma_frac_fp4": round(tot_flops / (tot_us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),
+        "config": {
+            "workload": "mxfp4_gemm, the six benchmark shapes: " + "; ".join(
+                shape_label(c) for c in cases),
+            "value_shape": shape_label(main_case),
+            "shapes": per,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": mp.get("hbm_bytes_per_call"),
+            "kernel": (main_kernel.get("name") or "gemm_kernel") + " at " + shape_label(main_case),
+            "kernel_us_mean": round(k_mean, 3), "basis": basis,
+            "event_us_mean": round(e_mean, 3),
+            "achieved_event": round(vb / (e_mean * 1e-6) / 1e9, 1),
+            "frac_event": round(vb / (e_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "fp4_mfma": {
+            "shape": shape_label(mfma_case), "peak_tflops": FP4_PEAK_TFLOPS,
+            "frac_kernel": m_us and round(mfl / (m_us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 5),
+            "frac_event": per[MFMA_SHAPE]["mfma_frac_event"],
+            "counters": mprof.get("mfma_counters"),
+        },
+        "event_floor_us": {"median": round(statistics.median(floor), 3),
+                           "min": round(min(floor), 3)},
+        "empty_kernel_us_rocprof": rec.get("empty_kernel_us"),
+        "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(names, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inputs.ORDER, VALUE_SHAPE, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
-    if args.all:
-        for n in inputs.ORDER:
-            c = Case(n, torch, mx)
-            us = time_cold(torch, flush, c.call, args.steps, args.warmup)
-            med = statistics.median(us)
-            b = alg_bytes(c.M, c.N, c.K)
-            alt = {}
-            for label, fields in ALTERNATIVES.get(n, {}).items():
-                p = mx.Plan(*fields)
-                ws = mx.new_workspace(mx.workspace_bytes(c.M, c.N, c.K, p), "cuda:0")
-                run = lambda: mx.gemm(c.a, c.b_packed, c.N, out=c.c, workspace=ws, plan=p)
-                alt[label] = {"plan": p.__dict__, "median_us": round(statistics.median(
-                    time_cold(torch, flush, run, args.steps, args.warmup)), 3)}
-            print(json.dumps({"shape": n, "plan": c.plan.__dict__, "median_us": round(med, 3),
-                              "mean_us": round(statistics.fmean(us), 3),
-                              "trimmed_mean_us": round(trimmed_mean(us), 3),
-                              "hbm_GBps": round(b / (med * 1e-6) / 1e9, 1),
-                              "mfma_frac_fp4": round(2 * c.M * c.N * c.K / (med * 1e-6) / 1e12
-                                                     / FP4_PEAK_TFLOPS, 5),
-                              "prepack_us": round(statistics.median(
-                                  time_cold(torch, flush, c.pack, 10, 2)), 3),
-                              "alternatives": alt}), flush=True)
-            del c
+    if args.alternatives:
+        for n, alts in ALTERNATIVES.items():
+            base = next(c for c in cases if c.name == n)
+            out = {"shape": n, "default": {"plan": base.plan.__dict__,
+                                           "median_us": per[n]["median_us"]}}
+            for label, fields in alts.items():
+                c = Case(n, torch, mx, plan=mx.Plan(*fields))
+                e, _ = time_cold(torch, flush, [c], args.steps, args.warmup)
+                out[label] = {"plan": c.plan.__dict__,
+                              "median_us": round(statistics.median(e[n]), 3)}
+                del c
+            print(json.dumps(out), flush=True)
 
     if args.large:
         for i, (M, N, K) in enumerate(LARGE):
             w = inputs.Workload("large_m%d_n%d_k%d" % (M, N, K), M, N, K, seed=100 + i)
             c = Case(w, torch, mx)
             steps = max(3, min(args.steps, 20))
-            us = time_cold(torch, flush, c.call, steps, 2)
+            e, _ = time_cold(torch, flush, [c], steps, 2)
             ap = mx.quant_a_packed(c.a)
             pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, plan=c.plan)
-            us_pre = time_cold(torch, flush, pre, steps, 2)
+            us_pre = time_cold_fn(torch, flush, pre, steps, 2)
             fl = 2.0 * M * N * K
-            med, med_pre = statistics.median(us), statistics.median(us_pre)
+            med, med_pre = statistics.median(e[w.name]), statistics.median(us_pre)
             print(json.dumps({"shape": w.name, "plan": c.plan.__dict__, "median_us": round(med, 3),
-                              "mfma_frac_fp4": round(fl / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                              "mfma_frac_event": round(fl / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
                               "prequant_A_median_us": round(med_pre, 3),
-                              "prequant_A_mfma_frac_fp4": round(
-                                  fl / (med_pre * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
-                              "hbm_GBps": round(alg_bytes(M, N, K) / (med * 1e-6) / 1e9, 1)}),
+                              "prequant_A_mfma_frac_event": round(
+                                  fl / (med_pre * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}),
                   flush=True)
             del c, ap
             torch.cuda.empty_cache()
