@@ -18,7 +18,8 @@ __all__ = [
     "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "MODE_TILED", "REDUCE_KERNEL", "REDUCE_LAST_WG",
     "REDUCE_ATOMIC", "library_path", "load", "packed_bytes",
     "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes",
-    "prequant_workspace_bytes", "new_workspace", "gemm", "gemm_prequant", "version",
+    "prequant_workspace_bytes", "new_workspace", "gemm", "gemm_noalloc", "noalloc_max_scratch_bytes",
+    "gemm_prequant", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +83,8 @@ _SIGNATURES = {
     "mxfp4_gemm": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "mxfp4_gemm_ex": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz,
                            ctypes.POINTER(_CPlan), _vp]),
+    "mxfp4_gemm_noalloc": (_i, [_vp, _i, _vp, _sz, _vp, _i, _i, _i, _i, _vp]),
+    "mxfp4_gemm_noalloc_max_scratch_bytes": (_sz, []),
     "mxfp4_gemm_prequant": (_i, [_vp, _sz, _vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz,
                                  ctypes.POINTER(_CPlan), _vp]),
     "mxfp4_last_error": (ctypes.c_char_p, []),
@@ -239,6 +242,22 @@ def gemm(a, b_packed, N, out=None, workspace=None, plan=None, stream=None):
                                 out.stride(0), M, N, K, _ptr(workspace),
                                 _nbytes(workspace) if workspace is not None else 0,
                                 ctypes.byref(cp) if cp is not None else None, _stream(stream)))
+    return out
+
+
+def noalloc_max_scratch_bytes():
+    """Bytes of the library's per-GPU scratch array used by gemm_noalloc."""
+    return int(load().mxfp4_gemm_noalloc_max_scratch_bytes())
+
+
+def gemm_noalloc(a, b_packed, N, out, stream=None):
+    """C = A . B^T with the default plan and no workspace: the scratch lives in
+    the library's per-GPU array (calls on one GPU must not overlap).  `out`
+    (bf16 [M, N] or wider rows) is required, so nothing is allocated here
+    either."""
+    M, K, lda = _rows(a)
+    _check(load().mxfp4_gemm_noalloc(_ptr(a), lda, _ptr(b_packed), _nbytes(b_packed), _ptr(out),
+                                     out.stride(0), M, N, K, _stream(stream)))
     return out
 
 

@@ -8,10 +8,21 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "mxfp4.h"
 #include "mx_internal.hpp"
+
+// ---------------------------------------------------- allocation-free entry
+// Device scratch of mxfp4_gemm_noalloc: a fixed array in the library's own
+// device code, one copy per GPU, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): each device's copy is looked up once with
+// hipGetSymbolAddress (device_scratch below), and that pointer is what the
+// kernels get.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -451,9 +462,13 @@ size_t mxfp4_gemm_workspace_bytes(int M, int N, int K) {
   return ws_layout(p, M, N, K, false).total();
 }
 
-int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
-                  uint16_t* c, int ldc, int M, int N, int K, void* workspace,
-                  size_t workspace_bytes, const mxfp4_plan* plan, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of mxfp4_gemm_ex that do not depend on the plan.
+int check_gemm_args(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
+                    const uint16_t* c, int ldc, int M, int N, int K) {
   int rc;
   if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(b_packed, "b_packed")) ||
       (rc = check_stream_ptrs(c, "c")))
@@ -466,6 +481,45 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
   const size_t bneed = mxfp4_packed_bytes(N, K);
   if (b_packed_bytes < bneed)
     return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
+  return MXFP4_OK;
+}
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// This device's scratch pointer (looked up on the device's first call).
+int device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MXFP4_EINVAL, "mxfp4_gemm_noalloc supports devices 0..%d (current device %d)",
+                kScratchDevices - 1, dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p || !aligned(p, 256)) return fail(MXFP4_EHIP, "scratch symbol has no usable address");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
+                  uint16_t* c, int ldc, int M, int N, int K, void* workspace,
+                  size_t workspace_bytes, const mxfp4_plan* plan, void* stream) {
+  int rc;
+  if ((rc = check_gemm_args(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K))) return rc;
   const mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
   if ((rc = check_plan(p, M, N, K, true))) return rc;
   const WsLayout wl = ws_layout(p, M, N, K, false);
@@ -498,6 +552,31 @@ int mxfp4_gemm(const uint16_t* a, int lda, const void* b_packed, size_t b_packed
                size_t workspace_bytes, void* stream) {
   return mxfp4_gemm_ex(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K, workspace,
                        workspace_bytes, nullptr, stream);
+}
+
+size_t mxfp4_gemm_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int mxfp4_gemm_noalloc(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
+                       uint16_t* c, int ldc, int M, int N, int K, void* stream) {
+  int rc;
+  if ((rc = check_gemm_args(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K))) return rc;
+  const mxfp4_plan p = default_plan(M, N, K);
+  if ((rc = check_plan(p, M, N, K, true))) return rc;
+  const WsLayout wl = ws_layout(p, M, N, K, false);
+  if (wl.total() > kNoAllocScratchBytes)
+    return fail(MXFP4_EWORKSPACE,
+                "the default plan for %dx%dx%d needs %zu bytes of scratch; mxfp4_gemm_noalloc "
+                "holds at most %zu (call mxfp4_gemm with a workspace instead)",
+                M, N, K, wl.total(), kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (wl.total() > 0 && (rc = device_scratch(&ws))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (wl.zero_bytes() > 0) {  // the previous call's contents stay in the array
+    hipError_t e = mx::launch_zero_fill(ws, wl.zero_bytes(), st);
+    if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
+  }
+  return mxfp4_gemm_ex(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K, ws, wl.total(), &p,
+                       stream);
 }
 
 int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void* b_packed,

@@ -512,6 +512,24 @@ __global__ __launch_bounds__(kRedThreads) void splitk_reduce_kernel(const float*
   }
 }
 
+// Zero-fill of a scratch prefix by plain vector stores (a fill kernel rather
+// than a memset node, so that a captured call replays it correctly).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* p, unsigned long long words) {
+  const unsigned long long stride = (unsigned long long)gridDim.x * blockDim.x;
+  for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += stride)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const unsigned long long words = bytes / 4;
+  const unsigned long long blocks = (words + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 4096 ? (blocks ? blocks : 1) : 4096);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ dispatch table
 
 #define MX_KSW_LIST(X, MODE, MBW, NTW) \

@@ -78,6 +78,9 @@ TiledGeom tiled_geometry(int M, int N, int K, int tile_n);
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
                              int M, int N, int K, int tile_n, hipStream_t stream);
 
+// Zero `bytes` bytes (a multiple of 4) at p with a fill kernel.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+
 void launch_quant_linear(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
                          uint8_t* out_scale, int ld_scale, hipStream_t stream);
 void launch_quant_packed(const uint16_t* a, int M, int K, int lda, uint8_t* out,

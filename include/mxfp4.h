@@ -238,6 +238,31 @@ int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_pac
                   uint16_t *c, int ldc, int M, int N, int K, void *workspace,
                   size_t workspace_bytes, const mxfp4_plan *plan, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): C = A . B^T
+ * with the default plan, as mxfp4_gemm, but with no workspace argument.  The
+ * scratch the plan needs (split-K partials, the pre-quantized A) lives in a
+ * fixed array inside the library, one copy per GPU, of
+ * mxfp4_gemm_noalloc_max_scratch_bytes() bytes (16 MiB), held from the
+ * library's first use of that GPU until the process ends; the call allocates
+ * and frees nothing.  Shapes whose default plan needs more scratch than that
+ * (mxfp4_gemm_workspace_bytes) are refused with MXFP4_EWORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array and
+ * the array keeps the last call's contents (parts that must start at zero
+ * are cleared by the call itself, with a fill kernel): calls on one GPU
+ * that may overlap in time -- on different streams, or from several threads
+ * without ordering -- race on it and give undefined results; serialize
+ * them, or use mxfp4_gemm with one workspace per stream.  Results are those
+ * of mxfp4_gemm bit for bit.  The first call on a GPU looks up that GPU's
+ * copy of the array (hipGetSymbolAddress).
+ * Arguments and errors: as mxfp4_gemm, plus EWORKSPACE for too large a
+ * shape. */
+int mxfp4_gemm_noalloc(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
+                       uint16_t *c, int ldc, int M, int N, int K, void *stream);
+
+/* Bytes of the per-GPU scratch array of mxfp4_gemm_noalloc. */
+size_t mxfp4_gemm_noalloc_max_scratch_bytes(void);
+
 /* Workspace bytes of mxfp4_gemm_prequant for a plan (NULL = default plan);
  * its zero-fill prefix is mxfp4_plan_workspace_zero_bytes of the same plan. */
 size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan *plan, int M, int N, int K);

@@ -266,3 +266,20 @@ def test_default_plan_mode_by_size(lib):
         p = mx.default_plan(M, N, K)
         assert p.mode == mx.MODE_TILED and (p.waves_n != 2) == wide, (M, N, K, p)
         assert mx.workspace_bytes(M, N, K) == mx.packed_bytes(M, K) + (-mx.packed_bytes(M, K) % 256)
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    """A shape whose default plan needs more scratch than the library's
+    per-GPU array is refused before any device call (so this runs on the
+    CPU); fake, aligned pointers are never dereferenced."""
+    cap = lib.mxfp4_gemm_noalloc_max_scratch_bytes()
+    assert cap == 16 << 20
+    M, N, K = 4096, 8192, 8192  # tiled plan: 17,825,792 bytes of pre-quantized A
+    assert lib.mxfp4_gemm_workspace_bytes(M, N, K) > cap
+    a, bp, c = 0x10000, 0x20000, 0x30000
+    rc = lib.mxfp4_gemm_noalloc(a, K, bp, mx.packed_bytes(N, K), c, N, M, N, K, None)
+    assert rc == EWORKSPACE
+    assert b"mxfp4_gemm with a workspace" in lib.mxfp4_last_error()
+    # argument errors come first, as for mxfp4_gemm
+    assert lib.mxfp4_gemm_noalloc(None, K, bp, mx.packed_bytes(N, K), c, N, M, N, K, None) == ENULL
+    assert lib.mxfp4_gemm_noalloc(a, K, bp, 16, c, N, 16, N, K, None) == ESIZE
