@@ -18,11 +18,13 @@ ORACLE = os.path.join(ROOT, "oracle")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-def build() -> str:
+def build(out: str = EXE, extra_flags=()) -> str:
     """Compile with every warning an error (-pedantic for the library's own
-    header; the HIP headers are system headers); returns the program path."""
-    tmp = EXE + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
+    header; the HIP headers are system headers); returns the program path.
+    `out` and `extra_flags` serve the sanitizer build (a separate program
+    next to the normal one, so that the rpath still finds the libraries)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic"] + list(extra_flags) + [
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
            "-isystem", os.path.join(ROCM, "include"), SRC, "-o", tmp,
            "-L", PKG, "-lmxfp4", "-L", ORACLE, "-loracle",
@@ -32,8 +34,8 @@ def build() -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("gcc failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, EXE)
-    return EXE
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
