@@ -24,11 +24,14 @@
  *     device, whose memory the device pointers must be; all device work is
  *     enqueued asynchronously on it and nothing is synchronised;
  *   - the library never allocates or frees device memory: the caller owns
- *     every buffer, and the size queries say how large each must be;
+ *     every buffer, and the size queries say how large each must be (the one
+ *     exception, mxfp4_gemm_noalloc, uses a fixed array inside the library
+ *     instead of a caller's workspace);
  *   - return value 0 is success; a negative value is one of MXFP4_E* below.
  *     On any error other than MXFP4_EHIP nothing has been enqueued.  The
  *     text of the last error of the calling thread is mxfp4_last_error();
- *   - calls are thread-safe; the library holds no per-call device state;
+ *   - calls are thread-safe; apart from mxfp4_gemm_noalloc's per-GPU
+ *     scratch array the library holds no device state between calls;
  *   - a call enqueues kernel launches only (no allocation, memset or
  *     synchronization), so it can be captured into a HIP graph; a replay
  *     reads the buffers as they are at replay time, and replays that share
