@@ -257,7 +257,9 @@ int mxfp4_gemm_ex(const uint16_t *a, int lda, const void *b_packed, size_t b_pac
  * without ordering -- race on it and give undefined results; serialize
  * them, or use mxfp4_gemm with one workspace per stream.  Results are those
  * of mxfp4_gemm bit for bit.  The first call on a GPU looks up that GPU's
- * copy of the array (hipGetSymbolAddress).
+ * copy of the array (hipGetSymbolAddress); make that call outside a HIP
+ * graph capture: every later call enqueues kernel launches only, so it can
+ * be captured like mxfp4_gemm.
  * Arguments and errors: as mxfp4_gemm, plus EWORKSPACE for too large a
  * shape. */
 int mxfp4_gemm_noalloc(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
