@@ -128,7 +128,11 @@ def build(jobs=None):
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_compile, SOURCES))
     objs = [o for o, _ in results]
-    kernels = write_report([k for _, ks in results for k in ks])
+    kernels = [k for _, ks in results for k in ks]
+    if not kernels:
+        raise RuntimeError("the compiler printed no kernel-resource-usage remarks; "
+                           "cannot check the kernels for scratch use")
+    kernels = write_report(kernels)
     print(summary(kernels))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
