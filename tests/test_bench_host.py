@@ -44,3 +44,19 @@ def test_alternative_plans_are_valid():
         w = inputs.WORKLOADS[name]
         for fields in alts.values():
             mx.check_plan(mx.Plan(*fields), w.M, w.N, w.K)
+
+
+def test_recorded_profile_matches_the_kernel_sources():
+    """profiles/traffic.json (the rocprofv3 record bench.py reads for kernel
+    durations, HBM bytes and counters) was taken with the current kernel
+    sources and covers every benchmark shape; a kernel change without a new
+    profile fails here, before a bench line reports stale figures."""
+    from block_scaled_precision_quant_amd import inputs
+    rec = bench.recorded_profiles()
+    assert rec, "profiles/traffic.json is missing or was taken with other kernel sources"
+    assert set(rec["shapes"]) == set(inputs.ORDER)
+    for name, e in rec["shapes"].items():
+        w = inputs.WORKLOADS[name]
+        assert e["alg_bytes"] == bench.alg_bytes(w.M, w.N, w.K)
+        assert e["kernel_us"] > 0 and e["hbm_bytes_per_call"] > 0
+    assert rec["empty_kernel_us"]["median"] > 0
