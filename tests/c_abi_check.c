@@ -7,8 +7,10 @@
  *                      B quantized by the CPU oracle (liboracle.so) and
  *                      repacked by mxfp4_pack_b, A quantized by the library
  *                      inside mxfp4_gemm; C checked against the oracle's fp32
- *                      sum elementwise (|d| <= 1e-2 |ref| + 1e-2), and
- *                      mxfp4_quant_a's bytes against the oracle's, exactly.
+ *                      sum elementwise (|d| <= 1e-2 |ref| + 1e-2),
+ *                      mxfp4_quant_a's bytes against the oracle's, exactly,
+ *                      and mxfp4_gemm_noalloc's C against mxfp4_gemm's, bit
+ *                      for bit.
  *
  * Exit status 0 when every check holds; a message names the first failure.
  */
@@ -72,6 +74,9 @@ static int host_checks(void) {
     CHECK(mxfp4_default_plan(32, 4096, 512, NULL) == MXFP4_ENULL, "NULL plan refused");
     CHECK(mxfp4_gemm(NULL, 512, NULL, 0, NULL, 4096, 32, 4096, 512, NULL, 0, NULL) == MXFP4_ENULL,
           "NULL pointers refused before any launch");
+    CHECK(mxfp4_gemm_noalloc(NULL, 512, NULL, 0, NULL, 4096, 32, 4096, 512, NULL) == MXFP4_ENULL,
+          "noalloc: NULL pointers refused");
+    CHECK(mxfp4_gemm_noalloc_max_scratch_bytes() == ((size_t)16 << 20), "noalloc scratch size");
     printf("host checks ok\n");
     return 0;
 }
@@ -119,8 +124,17 @@ static int gpu_check(void) {
           "gemm: %s", mxfp4_last_error());
     CHECK(mxfp4_quant_a(da, M, K, K, dq, K / 2, ds, K / 32, NULL) == MXFP4_OK, "quant_a: %s",
           mxfp4_last_error());
+    /* the allocation-free entry on the same operands: the same bits */
+    void *dc2;
+    uint16_t *c2 = malloc((size_t)M * N * 2);
+    CHECK(c2 != NULL, "host allocation");
+    HIP(hipMalloc(&dc2, (size_t)M * N * 2));
+    CHECK(mxfp4_gemm_noalloc(da, K, dbp, bp_bytes, dc2, N, M, N, K, NULL) == MXFP4_OK,
+          "gemm_noalloc: %s", mxfp4_last_error());
     HIP(hipDeviceSynchronize());
     HIP(hipMemcpy(c, dc, (size_t)M * N * 2, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(c2, dc2, (size_t)M * N * 2, hipMemcpyDeviceToHost));
+    CHECK(memcmp(c, c2, (size_t)M * N * 2) == 0, "gemm_noalloc differs from gemm");
     HIP(hipMemcpy(gq, dq, na / 2, hipMemcpyDeviceToHost));
     HIP(hipMemcpy(gs, ds, na / 32, hipMemcpyDeviceToHost));
 
@@ -143,6 +157,8 @@ static int gpu_check(void) {
     hipFree(dbs);
     hipFree(dbp);
     hipFree(dc);
+    hipFree(dc2);
+    free(c2);
     hipFree(dq);
     hipFree(ds);
     if (dws) hipFree(dws);
