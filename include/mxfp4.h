@@ -226,7 +226,9 @@ size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
  *             leading zero-bytes (see mxfp4_plan_workspace_zero_bytes) were
  *             zero-filled once before first use.
  * Requires M >= 1, N >= 1, K >= 32, K % 32 == 0.
- * Inputs are finite.  Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
+ * Inputs are finite.  c must not overlap a, b_packed or the workspace (the
+ * kernels read the inputs while other workgroups already write C).
+ * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */
 int mxfp4_gemm(const uint16_t *a, int lda, const void *b_packed, size_t b_packed_bytes,
                uint16_t *c, int ldc, int M, int N, int K, void *workspace,
                size_t workspace_bytes, void *stream);
