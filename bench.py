@@ -317,8 +317,11 @@ def main(argv=None):
     prof = rec.get("shapes", {})
     per = {c.name: summarize(c, ev[c.name], prof) for c in cases}
     for c in cases:
-        per[c.name]["prepack_us"] = round(statistics.median(
-            time_cold_fn(torch, flush, c.pack, 10, 2)), 3)
+        pp = statistics.median(time_cold_fn(torch, flush, c.pack, 10, 2))
+        per[c.name]["prepack_us"] = round(pp, 3)
+        # the one-time repack reads and writes N*K/2 + N*K/32 bytes
+        per[c.name]["prepack_GBps_event"] = round(2 * (c.N * c.K // 2 + c.N * c.K // 32)
+                                                  / (pp * 1e-6) / 1e9, 1)
 
     # the same protocol around the smallest kernel there is (a 1-element
     # fill): the event-time floor of one launch after the cache eviction
