@@ -9,6 +9,11 @@ current torch stream becomes the HIP stream, and every computation runs in
 the library's HIP kernels.  There is no fallback path: if the library is
 missing or a call fails, an exception is raised.  The C functions and their
 contracts are declared in include/mxfp4.h.
+
+Before a pointer is passed on, each tensor is checked for what the C
+functions cannot see: that it lives on a GPU, its dtype, and a shape and
+strides whose memory covers everything the call reads or writes (a tensor
+that fails raises TypeError or ValueError and nothing is launched).
 """
 import ctypes
 import os
@@ -132,6 +137,39 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _gpu(t, name, dtype=None, like=None):
+    """`t` is a GPU tensor (of `dtype`, on the device of `like` when given)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor (got %s)" % (name, type(t).__name__))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU (got device %s)" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if like is not None and t.device != like.device:
+        raise ValueError("%s is on %s, the other operands on %s" % (name, t.device, like.device))
+    return t
+
+
+def _flat(t, name, dtype=None, like=None):
+    """A buffer passed as pointer + byte count: its bytes must be contiguous."""
+    _gpu(t, name, dtype, like)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (its size is passed in bytes)" % name)
+    return t
+
+
+def _matrix(t, name, dtype, rows, cols, like=None):
+    """A [rows, cols] matrix with unit stride along cols; its row stride is the
+    leading dimension passed on (the C functions check it against cols)."""
+    _gpu(t, name, dtype, like)
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError("%s must have shape (%d, %d) (got %s)" % (name, rows, cols, tuple(t.shape)))
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit stride along its second dimension" % name)
+    return t
+
+
 def version():
     return load().mxfp4_version().decode()
 
@@ -145,18 +183,27 @@ def pack_b(b_fp4, b_scale, out=None, stream=None):
     """Repack linear fp4x2 [N, K/2] + e8m0 [N, K/32] (uint8 CUDA tensors) into
     the MX-packed layout; returns the uint8 buffer."""
     import torch
+    _flat(b_fp4, "b_fp4", torch.uint8)
+    if b_fp4.dim() != 2:
+        raise ValueError("b_fp4 must be 2-D [N, K/2] (got %s)" % (tuple(b_fp4.shape),))
     N, half = b_fp4.shape
     K = 2 * half
+    _flat(b_scale, "b_scale", torch.uint8, like=b_fp4)
+    if tuple(b_scale.shape) != (N, K // 32):
+        raise ValueError("b_scale must have shape (%d, %d) (got %s)" % (N, K // 32, tuple(b_scale.shape)))
     if out is None:
         out = torch.empty(packed_bytes(N, K), dtype=torch.uint8, device=b_fp4.device)
+    _flat(out, "out", like=b_fp4)
     _check(load().mxfp4_pack_b(_ptr(b_fp4), _ptr(b_scale), N, K, _ptr(out), _nbytes(out),
                                _stream(stream)))
     return out
 
 
 def _rows(a):
-    if a.dim() != 2 or a.stride(1) != 1:
-        raise ValueError("A must be a 2-D tensor with unit stride along K")
+    import torch
+    _gpu(a, "a", torch.bfloat16)
+    if a.dim() != 2 or (a.shape[1] > 1 and a.stride(1) != 1):
+        raise ValueError("a must be a 2-D tensor with unit stride along K")
     return a.shape[0], a.shape[1], a.stride(0)
 
 
@@ -168,6 +215,8 @@ def quant_a(a, out_fp4=None, out_scale=None, stream=None):
         out_fp4 = torch.empty((M, K // 2), dtype=torch.uint8, device=a.device)
     if out_scale is None:
         out_scale = torch.empty((M, K // 32), dtype=torch.uint8, device=a.device)
+    _matrix(out_fp4, "out_fp4", torch.uint8, M, K // 2, like=a)
+    _matrix(out_scale, "out_scale", torch.uint8, M, K // 32, like=a)
     _check(load().mxfp4_quant_a(_ptr(a), M, K, lda, _ptr(out_fp4), out_fp4.stride(0),
                                 _ptr(out_scale), out_scale.stride(0), _stream(stream)))
     return out_fp4, out_scale
@@ -179,6 +228,7 @@ def quant_a_packed(a, out=None, stream=None):
     M, K, lda = _rows(a)
     if out is None:
         out = torch.empty(packed_bytes(M, K), dtype=torch.uint8, device=a.device)
+    _flat(out, "out", like=a)
     _check(load().mxfp4_quant_a_packed(_ptr(a), M, K, lda, _ptr(out), _nbytes(out),
                                        _stream(stream)))
     return out
@@ -224,8 +274,10 @@ def new_workspace(nbytes, device):
 
 
 def _workspace(nbytes, device, workspace):
-    if nbytes == 0 or workspace is not None:
-        return workspace
+    if workspace is not None:
+        return _flat(workspace, "workspace")
+    if nbytes == 0:
+        return None
     return new_workspace(nbytes, device)
 
 
@@ -234,9 +286,13 @@ def gemm(a, b_packed, N, out=None, workspace=None, plan=None, stream=None):
     Returns bf16 [M, N] (written into `out` when given)."""
     import torch
     M, K, lda = _rows(a)
+    _flat(b_packed, "b_packed", like=a)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _matrix(out, "out", torch.bfloat16, M, N, like=a)
     workspace = _workspace(workspace_bytes(M, N, K, plan), a.device, workspace)
+    if workspace is not None:
+        _gpu(workspace, "workspace", like=a)
     cp = plan._c() if plan is not None else None
     _check(load().mxfp4_gemm_ex(_ptr(a), lda, _ptr(b_packed), _nbytes(b_packed), _ptr(out),
                                 out.stride(0), M, N, K, _ptr(workspace),
@@ -255,7 +311,10 @@ def gemm_noalloc(a, b_packed, N, out, stream=None):
     the library's per-GPU array (calls on one GPU must not overlap).  `out`
     (bf16 [M, N] or wider rows) is required, so nothing is allocated here
     either."""
+    import torch
     M, K, lda = _rows(a)
+    _flat(b_packed, "b_packed", like=a)
+    _matrix(out, "out", torch.bfloat16, M, N, like=a)
     _check(load().mxfp4_gemm_noalloc(_ptr(a), lda, _ptr(b_packed), _nbytes(b_packed), _ptr(out),
                                      out.stride(0), M, N, K, _stream(stream)))
     return out
@@ -264,10 +323,15 @@ def gemm_noalloc(a, b_packed, N, out, stream=None):
 def gemm_prequant(a_packed, M, b_packed, N, K, out=None, workspace=None, plan=None, stream=None):
     """C = A . B^T with A already MX-packed (from quant_a_packed)."""
     import torch
+    _flat(a_packed, "a_packed")
+    _flat(b_packed, "b_packed", like=a_packed)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_packed.device)
+    _matrix(out, "out", torch.bfloat16, M, N, like=a_packed)
     p = plan if plan is not None else default_plan(M, N, K)
     workspace = _workspace(prequant_workspace_bytes(M, N, K, p), a_packed.device, workspace)
+    if workspace is not None:
+        _gpu(workspace, "workspace", like=a_packed)
     cp = p._c()
     _check(load().mxfp4_gemm_prequant(_ptr(a_packed), _nbytes(a_packed), _ptr(b_packed),
                                       _nbytes(b_packed), _ptr(out), out.stride(0), M, N, K,
