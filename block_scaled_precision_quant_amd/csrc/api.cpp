@@ -127,13 +127,16 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
     return bad(MXFP4_ENOTSUP,
                 "no kernel for m_blocks=%d n_tiles_per_wave=%d k_steps_per_wave=%d in this library",
                 p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave);
+  // each factor is bounded before any product is formed, so absurd field
+  // values cannot overflow the arithmetic below
+  const long long waves = (long long)p.waves_n * p.waves_k;
+  if (waves > mx::kMaxThreads / 64)
+    return bad(MXFP4_EINVAL, "plan has %lld wavefronts per workgroup (max %d)", waves,
+                mx::kMaxThreads / 64);
   const int KS = (int)(((long long)K + 127) / 128);
-  if ((long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
+  if (p.split_k > KS || (long long)p.split_k * p.waves_k * p.k_steps_per_wave != KS)
     return bad(MXFP4_EINVAL, "plan covers %lld K steps, shape has %d (split_k*waves_k*k_steps_per_wave must equal ceil(K/128))",
                 (long long)p.split_k * p.waves_k * p.k_steps_per_wave, KS);
-  if (p.waves_n * p.waves_k > mx::kMaxThreads / 64)
-    return bad(MXFP4_EINVAL, "plan has %d wavefronts per workgroup (max %d)", p.waves_n * p.waves_k,
-                mx::kMaxThreads / 64);
   mx::Plan q = to_internal(p);
   q.mode = mode;
   const mx::GemmGeom g = mx::gemm_geometry(q, M, N, K);

@@ -18,13 +18,11 @@ ORACLE = os.path.join(ROOT, "oracle")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-def build(out: str = EXE, extra_flags=()) -> str:
+def build(out: str = EXE) -> str:
     """Compile with every warning an error (-pedantic for the library's own
-    header; the HIP headers are system headers); returns the program path.
-    `out` and `extra_flags` serve the sanitizer build (a separate program
-    next to the normal one, so that the rpath still finds the libraries)."""
+    header; the HIP headers are system headers); returns the program path."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic"] + list(extra_flags) + [
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic"] + [
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
            "-isystem", os.path.join(ROCM, "include"), SRC, "-o", tmp,
            "-L", PKG, "-lmxfp4", "-L", ORACLE, "-loracle",

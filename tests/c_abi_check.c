@@ -74,6 +74,24 @@ static int host_checks(void) {
     CHECK(mxfp4_default_plan(32, 4096, 512, NULL) == MXFP4_ENULL, "NULL plan refused");
     CHECK(mxfp4_gemm(NULL, 512, NULL, 0, NULL, 4096, 32, 4096, 512, NULL, 0, NULL) == MXFP4_ENULL,
           "NULL pointers refused before any launch");
+    /* plan fields far out of range are refused without overflowing the
+     * checks' arithmetic (the sanitizer build traps signed overflow) */
+    mxfp4_plan huge = p; /* K = 512: 4 steps of 128 */
+    huge.waves_n = 1 << 30;
+    huge.waves_k = 4;
+    huge.k_steps_per_wave = 1;
+    huge.split_k = 1;
+    CHECK(mxfp4_check_plan(&huge, 32, 4096, 512) == MXFP4_EINVAL, "huge waves_n refused");
+    huge.waves_n = 2;
+    huge.waves_k = 1 << 30;
+    huge.k_steps_per_wave = 4;
+    huge.split_k = 1 << 30;
+    CHECK(mxfp4_check_plan(&huge, 32, 4096, 512) == MXFP4_EINVAL, "huge waves_k and split refused");
+    huge = p;
+    huge.split_k = 0x7FFFFFFF;
+    CHECK(mxfp4_check_plan(&huge, 32, 4096, 512) == MXFP4_EINVAL, "huge split refused");
+    huge.split_reduce = MXFP4_REDUCE_ATOMIC;
+    CHECK(mxfp4_plan_workspace_bytes(&huge, 32, 4096, 512) == 0, "no workspace for a huge split");
     CHECK(mxfp4_gemm_noalloc(NULL, 512, NULL, 0, NULL, 4096, 32, 4096, 512, NULL) == MXFP4_ENULL,
           "noalloc: NULL pointers refused");
     CHECK(mxfp4_gemm_noalloc_max_scratch_bytes() == ((size_t)16 << 20), "noalloc scratch size");

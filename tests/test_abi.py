@@ -94,6 +94,10 @@ def test_plan_checks(lib):
     assert check(mx.Plan(1, 4, 1, 2, 1, 5, 1)) == ENOTSUP       # k_steps_per_wave
     assert check(mx.Plan(1, 4, 1, 2, 1, 8, 1)) == EINVAL        # covers 8 of 16 steps
     assert check(mx.Plan(1, 1, 1, 8, 2, 8, 1)) == EINVAL        # 16 wavefronts
+    # fields far out of range: refused, no overflow in the checks' products
+    assert check(mx.Plan(1, 1, 1, 1 << 30, 1 << 30, 16, 1)) == EINVAL
+    assert check(mx.Plan(1, 1, 1, 2, 1 << 30, 16, 1 << 30)) == EINVAL
+    assert check(mx.Plan(1, 1, 1, 2, 1, 16, 0x7FFFFFFF, 2)) == EINVAL
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 0)) == 0         # reduce kernel: any split
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 16, 1)) == 0         # last-WG reduce: split <= 16
     assert check(mx.Plan(1, 1, 1, 1, 1, 1, 32, 1), k=4096) == EINVAL
