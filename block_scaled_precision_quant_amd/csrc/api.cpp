@@ -191,7 +191,8 @@ WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry
 // fitted picks are within 7 % of the best plan on each): each workgroup
 // streams its A rows (bf16 when fused, fp4 + scales when pre-quantized) and
 // B columns (fp4 + scales) for its K range at up to 100 GB/s per CU, less
-// with fewer than eight wavefronts, and in fused mode quantizes its A rows
+// with fewer than eight wavefronts (fused mode: whole 16-row blocks of bf16
+// A, whatever M), and in fused mode quantizes its A rows
 // (about 2 us per 64 Ki elements); each further 256 workgroups is another
 // round; a split-K adds the reduce launch, its partials and a little per
 // slice; pre-quantized A adds the quantizer launch and its traffic; a small
@@ -207,7 +208,10 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
   const double kel = 128.0 * p.waves_k * p.k_steps_per_wave;
   const bool fused = p.mode == MXFP4_MODE_FUSED;
   const double a_bytes = fused ? 2.0 : 17.0 / 32.0;  // per element
-  const double bytes = rows * kel * a_bytes + cols * kel * 17.0 / 32.0;
+  // fused mode loads whole 16-row blocks of A (rows past M repeat earlier
+  // rows, so the load count is fixed), and each load costs its issue
+  const double a_rows = fused ? 16.0 * p.m_blocks : rows;
+  const double bytes = a_rows * kel * a_bytes + cols * kel * 17.0 / 32.0;
   const int waves = p.waves_n * p.waves_k;
   const double rate = 100000.0 * fmin(1.0, pow(waves / 8.0, 0.75));  // bytes per us
   double t = rounds * bytes / rate;
