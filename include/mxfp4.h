@@ -169,7 +169,8 @@ typedef struct mxfp4_plan {
     int m_blocks;         /* 16-row blocks of A per workgroup: 1, 2 or 4 */
     int n_tiles_per_wave; /* 16-column tiles of B per wavefront: 1 or 2 */
     int waves_n;          /* wavefronts along N per workgroup */
-    int waves_k;          /* wavefronts along K per workgroup (in-LDS reduce) */
+    int waves_k;          /* wavefronts along K per workgroup (in-LDS reduce);
+                             waves_n * waves_k <= 8 */
     int k_steps_per_wave; /* 128-K steps per wavefront: 1,2,3,4,6,7,8,12,14,16 */
     int split_k;          /* workgroups along K (fp32 workspace + reduce) */
     int split_reduce;     /* split_k > 1: MXFP4_REDUCE_KERNEL, MXFP4_REDUCE_LAST_WG
