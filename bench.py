@@ -20,13 +20,14 @@ against the HBM peak: algorithmic bytes over the kernel's traced duration
 is the compute-leaning 256x3072x1536 shape against the dense FP4 peak.
 `ms_per_step` is wall time per step, cache-evicting fills included.
 
-  python bench.py [--steps K] [--warmup W] [--alternatives] [--large]
+  python bench.py [--steps K] [--warmup W] [--alternatives] [--large] [--stream]
                   [--no-cpu-baseline] [--cpu-seconds S] [--copy-calibration]
 
 --alternatives adds one line per shape that has a choice, timing the other
 plans (A pre-quantized by a separate launch, the tiled kernel) the same way.
 --large adds one line per large shape (M >= 1024), whose default plan is the
-tiled kernel.
+tiled kernel.  --stream adds one line per weight-streaming shape (small M, a
+B of 60-150 MB), timed through the default plan the same way.
 """
 import argparse
 import json
@@ -74,6 +75,8 @@ def parse(argv=None):
                     help="one extra JSON line per shape with a plan choice")
     ap.add_argument("--large", action="store_true",
                     help="one extra JSON line per large shape (tiled kernel)")
+    ap.add_argument("--stream", action="store_true",
+                    help="one extra JSON line per weight-streaming shape (small M, large N x K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=3.0,
                     help="wall seconds of the all-cores oracle run (plus one single-thread "
@@ -86,6 +89,9 @@ def parse(argv=None):
 
 # large shapes for --large: (M, N, K), seeded like the workloads
 LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
+# weight-streaming shapes for --stream: (M, N, K), B of 60-150 MB
+STREAM = [(1, 16384, 16384), (16, 16384, 16384), (64, 16384, 16384), (32, 28672, 8192),
+          (16, 8192, 28672)]
 
 # --alternatives: the other plans where a shape makes a choice -- the fastest
 # pre-quantized-A plan of an L2-cold sweep over every valid plan (a separate
@@ -421,6 +427,33 @@ def main(argv=None):
                                   fl / (med_pre * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}),
                   flush=True)
             del c, ap
+            torch.cuda.empty_cache()
+
+    if args.stream:
+        dev = torch.device("cuda:0")
+        for i, (M, N, K) in enumerate(STREAM):
+            # seeded normal inputs drawn on the device (B alone is up to 512 MiB of bf16)
+            gen = torch.Generator(device=dev).manual_seed(200 + i)
+            a = torch.randn((M, K), dtype=torch.bfloat16, device=dev, generator=gen)
+            b = torch.randn((N, K), dtype=torch.bfloat16, device=dev, generator=gen)
+            bq, bs = mx.quant_a(b)
+            del b
+            bp = mx.pack_b(bq, bs)
+            del bq, bs
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            plan = mx.default_plan(M, N, K)
+            nws = mx.workspace_bytes(M, N, K, plan)
+            ws = mx.new_workspace(nws, dev) if nws else None
+            us = time_cold_fn(torch, flush, lambda: mx.gemm(a, bp, N, out=c, workspace=ws, plan=plan),
+                              max(3, min(args.steps, 20)), 2)
+            med = statistics.median(us)
+            ab = alg_bytes(M, N, K)
+            print(json.dumps({"shape": "stream_m%d_n%d_k%d" % (M, N, K), "plan": plan.__dict__,
+                              "median_us": round(med, 3), "alg_bytes": ab,
+                              "alg_TBps_event": round(ab / med / 1e6, 3),
+                              "hbm_frac_event": round(ab / med / 1e3 / HBM_PEAK_GBPS, 4)}),
+                  flush=True)
+            del a, bp, c, ws
             torch.cuda.empty_cache()
 
 

@@ -44,6 +44,8 @@ def test_alternative_plans_are_valid():
         w = inputs.WORKLOADS[name]
         for fields in alts.values():
             mx.check_plan(mx.Plan(*fields), w.M, w.N, w.K)
+    for M, N, K in bench.LARGE + bench.STREAM:  # the extra lines' default plans
+        mx.check_plan(mx.default_plan(M, N, K), M, N, K)
 
 
 def test_recorded_profile_matches_the_kernel_sources():
