@@ -20,7 +20,8 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "MODE_TILED", "REDUCE_KERNEL", "REDUCE_LAST_WG",
+    "Mxfp4Error", "Plan", "MODE_FUSED", "MODE_PREQUANT", "MODE_TILED", "MODE_STREAM", "REDUCE_KERNEL",
+    "REDUCE_LAST_WG",
     "REDUCE_ATOMIC", "library_path", "load", "packed_bytes",
     "pack_b", "quant_a", "quant_a_packed", "default_plan", "check_plan", "workspace_bytes", "workspace_zero_bytes",
     "prequant_workspace_bytes", "new_workspace", "gemm", "gemm_noalloc", "noalloc_max_scratch_bytes",
@@ -31,6 +32,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 MODE_FUSED = 1
 MODE_PREQUANT = 2
 MODE_TILED = 3  # 32x32x64 instruction; waves_n == 2: 256 x 128 tiles, else 256 x 256; other fields ignored
+MODE_STREAM = 4  # K loop inside the workgroup: waves_n 4, waves_k 1, k_steps_per_wave = steps per workgroup
 REDUCE_KERNEL = 0
 REDUCE_LAST_WG = 1
 REDUCE_ATOMIC = 2

@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4.so")
 REPORT = os.path.join(BUILD, "kernel_resources.txt")
-SOURCES = ["quant.hip", "gemm.hip", "gemm_tiled.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_tiled.hip", "gemm_stream.hip", "api.cpp"]
 HEADERS = ["mx_device.hpp", "mx_internal.hpp"]
 ARCH = "gfx950"
 

@@ -92,16 +92,49 @@ int check_gemm_shape(int M, int N, int K) {
 // wavefronts), any other value 256 x 256 (eight).
 int tiled_width(const mxfp4_plan& p) { return p.waves_n == 2 ? 128 : 256; }
 
+// Stream-mode plan rules: four wavefronts along N, k_steps_per_wave is the
+// workgroup's K range in steps (a multiple of 4), and split_k the number of
+// workgroups that cover K with it.
+int check_stream_plan(const mxfp4_plan& p, int M, int N, int K, int (*bad)(int, const char*, ...)) {
+  if (!mx::stream_kernel_available(p.m_blocks, p.n_tiles_per_wave))
+    return bad(MXFP4_ENOTSUP, "MXFP4_MODE_STREAM has no kernel for m_blocks=%d n_tiles_per_wave=%d",
+               p.m_blocks, p.n_tiles_per_wave);
+  if (p.waves_n != 4 || p.waves_k != 1)
+    return bad(MXFP4_EINVAL, "MXFP4_MODE_STREAM runs four wavefronts along N (waves_n = 4, waves_k = 1)");
+  if (K > mx::kStreamMaxK)
+    return bad(MXFP4_EINVAL, "MXFP4_MODE_STREAM supports K <= %d (got %d)", mx::kStreamMaxK, K);
+  const int KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
+  if (p.k_steps_per_wave < 4 || p.k_steps_per_wave % 4 != 0 || p.k_steps_per_wave / 4 > KG)
+    return bad(MXFP4_EINVAL,
+               "MXFP4_MODE_STREAM: k_steps_per_wave is the workgroup's K steps, a multiple of 4 "
+               "in [4, %d] (got %d)", 4 * KG, p.k_steps_per_wave);
+  const int chunks = p.k_steps_per_wave / 4;
+  const int split = (KG + chunks - 1) / chunks;
+  if (p.split_k != split)
+    return bad(MXFP4_EINVAL, "MXFP4_MODE_STREAM: %d steps per workgroup need split_k = %d (got %d)",
+               p.k_steps_per_wave, split, p.split_k);
+  if (split > 1 && p.split_reduce != MXFP4_REDUCE_KERNEL)
+    return bad(MXFP4_EINVAL, "MXFP4_MODE_STREAM sums split partials with the reduce kernel only");
+  const mx::StreamGeom g = mx::stream_geometry(p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave, M, N, K);
+  if (g.grid * g.threads > 0xFFFFFFFFLL)
+    return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", g.grid, g.threads);
+  if (split > 1) {
+    const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
+    if (n > 0xFFFFFFFFLL - 63) return bad(MXFP4_EINVAL, "split-K reduce grid too large (%lld threads)", n);
+  }
+  return MXFP4_OK;
+}
+
 // Checks a plan against a shape; `mode_matters` is false for the prequant
-// entry point, where the mode only selects the tiled kernel or not.
+// entry point, where the mode only selects the tiled or stream kernel or not.
 int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
                bool report = true) {
   int (*const bad)(int, const char*, ...) = report ? fail : quiet;
   if (mode_matters && p.mode != MXFP4_MODE_FUSED && p.mode != MXFP4_MODE_PREQUANT &&
-      p.mode != MXFP4_MODE_TILED)
+      p.mode != MXFP4_MODE_TILED && p.mode != MXFP4_MODE_STREAM)
     return bad(MXFP4_EINVAL,
-               "plan.mode must be MXFP4_MODE_FUSED, MXFP4_MODE_PREQUANT or MXFP4_MODE_TILED (got %d)",
-               p.mode);
+               "plan.mode must be MXFP4_MODE_FUSED, _PREQUANT, _TILED or _STREAM (got %d)", p.mode);
+  if (p.mode == MXFP4_MODE_STREAM) return check_stream_plan(p, M, N, K, bad);
   if (p.mode == MXFP4_MODE_TILED) {
     // waves_n picks the tile width; the other fields are not used
     if (K > mx::kTiledMaxK)
@@ -168,6 +201,11 @@ struct WsLayout {
 WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
   WsLayout w = {0, 0, 0, false};
   if (p.mode == MXFP4_MODE_TILED) {
+    if (!prequant_entry) w.a = round_up(mxfp4_packed_bytes(M, K), 256);
+    return w;
+  }
+  if (p.mode == MXFP4_MODE_STREAM) {
+    if (p.split_k > 1) w.partials = round_up((size_t)p.split_k * M * N * 4, 256);
     if (!prequant_entry) w.a = round_up(mxfp4_packed_bytes(M, K), 256);
     return w;
   }
@@ -320,7 +358,36 @@ mxfp4_plan cached_model_plan(int M, int N, int K) {
   return p;
 }
 
-// Per-shape table for the tuned shapes, the cost model otherwise.
+// Stream mode for long K and a large B below M = 256 (a rule measured
+// L2-cold against the cost model's pick on 91 shapes, M 1..256, N x K 17M ..
+// 268M: it is taken where the stream kernel was faster on every measured
+// shape of its class -- 1.1-1.9x with M >= 96 and N x K >= 55M, 1.05-1.5x
+// with M >= 32 and either N >= 16384 or N x K >= 200M -- and left out where
+// it lost, below those sizes or with M < 32).
+bool use_stream(int M, int N, int K) {
+  const long long nk = (long long)N * K;
+  if (M > 255 || K < 4096 || nk < 55LL * 1000 * 1000) return false;
+  return M >= 96 || (M >= 32 && (N >= 16384 || nk >= 200LL * 1000 * 1000));
+}
+
+// The stream plan: every row block of up to 64 rows in one workgroup (one
+// block or two for M <= 32), 16-column tiles per wavefront (two for 65..128
+// rows and N >= 16384, where that measured faster), and the smallest split
+// of K that gives 192 workgroups or more.
+mxfp4_plan stream_plan(int M, int N, int K) {
+  const int MT = (M + 15) / 16, KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
+  const long long NT = ((long long)N + 15) / 16;
+  const int mbw = MT <= 2 ? MT : 4;
+  const int ntw = (MT >= 5 && MT <= 8 && N >= 16384) ? 2 : 1;
+  const long long mg = (MT + mbw - 1) / mbw, ng = (NT + 4 * ntw - 1) / (4 * ntw);
+  int split = 1;
+  while (ng * mg * split < 192 && split < KG) ++split;
+  const int chunks = (KG + split - 1) / split;
+  return make_plan(MXFP4_MODE_STREAM, mbw, ntw, 4, 1, 4 * chunks, (KG + chunks - 1) / chunks);
+}
+
+// Per-shape table for the tuned shapes, the stream rule, the cost model
+// otherwise.
 mxfp4_plan default_plan(int M, int N, int K) {
   struct Row {
     int M, N, K;
@@ -339,7 +406,10 @@ mxfp4_plan default_plan(int M, int N, int K) {
   };
   for (const Row& r : table)
     if (r.M == M && r.N == N && r.K == K) return r.p;
-
+  if (use_stream(M, N, K)) {
+    const mxfp4_plan p = stream_plan(M, N, K);
+    if (check_plan(p, M, N, K, true, false) == MXFP4_OK) return p;
+  }
   return cached_model_plan(M, N, K);
 }
 
@@ -458,7 +528,7 @@ size_t mxfp4_plan_workspace_zero_bytes(const mxfp4_plan* plan, int M, int N, int
 size_t mxfp4_gemm_prequant_workspace_bytes(const mxfp4_plan* plan, int M, int N, int K) {
   if (check_gemm_shape(M, N, K) != MXFP4_OK) return 0;
   mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
-  if (p.mode != MXFP4_MODE_TILED) p.mode = MXFP4_MODE_PREQUANT;
+  if (p.mode != MXFP4_MODE_TILED && p.mode != MXFP4_MODE_STREAM) p.mode = MXFP4_MODE_PREQUANT;
   if (check_plan(p, M, N, K, false) != MXFP4_OK) return 0;
   return ws_layout(p, M, N, K, true).total();
 }
@@ -534,7 +604,7 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const void* a_src = a;
-  if (p.mode == MXFP4_MODE_PREQUANT || p.mode == MXFP4_MODE_TILED) {
+  if (p.mode == MXFP4_MODE_PREQUANT || p.mode == MXFP4_MODE_TILED || p.mode == MXFP4_MODE_STREAM) {
     mx::launch_quant_packed(a, M, K, lda, ws + wl.a_off(), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "quant_a_packed launch");
@@ -545,6 +615,14 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
                                          tiled_width(p), st);
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
+    return ok();
+  }
+  if (p.mode == MXFP4_MODE_STREAM) {
+    hipError_t e = mx::launch_gemm_stream(p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave,
+                                          static_cast<const uint8_t*>(a_src),
+                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
+                                          reinterpret_cast<float*>(ws + wl.part_off()), st);
+    if (e != hipSuccess) return hip_fail(e, "gemm_stream launch");
     return ok();
   }
   hipError_t e = mx::launch_gemm(to_internal(p), a_src, lda, static_cast<const uint8_t*>(b_packed), c,
@@ -604,7 +682,7 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
   if (b_packed_bytes < bneed)
     return fail(MXFP4_ESIZE, "b_packed holds %zu bytes, layout needs %zu", b_packed_bytes, bneed);
   mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
-  if (p.mode != MXFP4_MODE_TILED) p.mode = MXFP4_MODE_PREQUANT;
+  if (p.mode != MXFP4_MODE_TILED && p.mode != MXFP4_MODE_STREAM) p.mode = MXFP4_MODE_PREQUANT;
   if ((rc = check_plan(p, M, N, K, false))) return rc;
   const WsLayout wl = ws_layout(p, M, N, K, true);
   if ((rc = check_workspace(workspace, workspace_bytes, wl.total()))) return rc;
@@ -614,6 +692,15 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
                                          tiled_width(p), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
+    return ok();
+  }
+  if (p.mode == MXFP4_MODE_STREAM) {
+    hipError_t e = mx::launch_gemm_stream(p.m_blocks, p.n_tiles_per_wave, p.k_steps_per_wave,
+                                          static_cast<const uint8_t*>(a_packed),
+                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
+                                          reinterpret_cast<float*>(ws + wl.part_off()),
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "gemm_stream launch");
     return ok();
   }
   hipError_t e = mx::launch_gemm(to_internal(p), a_packed, 0, static_cast<const uint8_t*>(b_packed), c,

@@ -655,14 +655,16 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
   hipError_t e = hipLaunchKernel(fn, dim3(geo.grid), dim3(geo.threads), kargs,
                                  (unsigned)geo.lds_total, stream);
   if (e != hipSuccess) return e;
-  if (p.split > 1 && p.reduce == kReduceKernel) {
-    const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
-    const unsigned grid = (unsigned)((n + kRedThreads - 1) / kRedThreads);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, ws, c, M, N,
-                       ldc, p.split);
-    e = hipGetLastError();
-  }
+  if (p.split > 1 && p.reduce == kReduceKernel) e = launch_splitk_reduce(ws, c, M, N, ldc, p.split, stream);
   return e;
+}
+
+hipError_t launch_splitk_reduce(const float* ws, uint16_t* c, int M, int N, int ldc, int S,
+                                hipStream_t stream) {
+  const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
+  const unsigned grid = (unsigned)((n + kRedThreads - 1) / kRedThreads);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, ws, c, M, N, ldc, S);
+  return hipGetLastError();
 }
 
 }  // namespace mx

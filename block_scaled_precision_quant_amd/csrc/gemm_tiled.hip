@@ -70,24 +70,6 @@ struct TiledArgs {
   int tiles_m, tiles_n, per_xcd;
 };
 
-// Raw buffer access: descriptor word 3 for untyped dword access on CDNA3/4;
-// reads past num_records return zero.
-typedef __amdgpu_buffer_rsrc_t BufRsrc;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kBufWord3 = 0x00020000;
-
-__device__ inline BufRsrc make_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kBufWord3);
-}
-// Asynchronous copy global -> LDS: lane L's 16 (or 4) bytes at voff + soff
-// land at lds + 16 L (or 4 L); lds is wave-uniform.
-typedef __attribute__((address_space(3))) void* LdsPtr;
-__device__ inline void dma16(BufRsrc r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, 0);
-}
-__device__ inline void dma4(BufRsrc r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 4, voff, soff, 0, 0);
-}
 
 // kSel selects the scale byte of sa and sb (the K step's position in its
 // group of four steps)

@@ -110,6 +110,27 @@ __device__ inline uint32_t encode8(uint4 v, uint32_t byte) {
   return r;
 }
 
+// ------------------------------------------------- buffer copies to LDS
+// Raw buffer access: descriptor word 3 for untyped dword access on CDNA3/4;
+// reads past num_records return zero.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ inline BufRsrc make_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kBufWord3);
+}
+// Asynchronous copy global -> LDS: lane L's 16 (or 4) bytes at voff + soff
+// land at lds + 16 L (or 4 L); lds is wave-uniform.
+typedef __attribute__((address_space(3))) void* LdsPtr;
+constexpr int kCachePolicyNT = 2;  // cache-policy operand of buffer loads: nontemporal
+__device__ inline void dma16(BufRsrc r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, 0);
+}
+__device__ inline void dma4(BufRsrc r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 4, voff, soff, 0, 0);
+}
+
 // ------------------------------------------------------ matrix instruction
 // One gfx950 block-scaled 16x16x128 FP4 x FP4 product-accumulate.
 //   a: this lane's 32 A codes (row L%16, K-group L/16), 16 bytes;

@@ -78,6 +78,29 @@ TiledGeom tiled_geometry(int M, int N, int K, int tile_n);
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
                              int M, int N, int K, int tile_n, hipStream_t stream);
 
+// Sum fp32 partials [S][M][N] in order s = 0..S-1 into bf16 C (gemm.hip).
+hipError_t launch_splitk_reduce(const float* ws, uint16_t* c, int M, int N, int ldc, int S,
+                                hipStream_t stream);
+
+// K-looping kernel on pre-quantized A (gemm_stream.hip): four wavefronts
+// along N, MBW row blocks, NTW tiles per wavefront, steps_per_wg 128-K steps
+// per workgroup (a multiple of 4), K split over ceil(ceil(KS/4) / chunks)
+// workgroups whose fp32 partials the reduce kernel sums.
+constexpr int kStreamMaxK = 1 << 22;  // buffer offsets within a workgroup's tiles stay below 2^31
+struct StreamGeom {
+  int MT, NT, KS, KG;
+  int chunks, split;   // 4-step chunks per workgroup, workgroups along K
+  int mgroups, ngroups;
+  long long grid;      // workgroups
+  int threads;
+  int lds;             // bytes of LDS per workgroup (static)
+};
+bool stream_kernel_available(int mbw, int ntw);
+StreamGeom stream_geometry(int mbw, int ntw, int steps_per_wg, int M, int N, int K);
+hipError_t launch_gemm_stream(int mbw, int ntw, int steps_per_wg, const uint8_t* a_packed,
+                              const uint8_t* b_packed, uint16_t* c, int ldc, int M, int N, int K,
+                              float* ws, hipStream_t stream);
+
 // Zero `bytes` bytes (a multiple of 4) at p with a fill kernel.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 

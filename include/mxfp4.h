@@ -155,17 +155,30 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * 256 x 256 tiles (eight wavefronts either way); both widths give the same
  * bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
  * many tiles.
+ *
+ * mode STREAM is the long-K kernel for small M: like PREQUANT it quantizes
+ * A into the workspace first; then each workgroup of four wavefronts (one
+ * group of n_tiles_per_wave 16-column tiles each) takes m_blocks 16-row
+ * blocks of A over a range of k_steps_per_wave 128-K steps (a multiple of
+ * 4, up to ceil(K/128) rounded up to 4), looping over it four steps at a
+ * time with the operands streamed through LDS, and split_k =
+ * ceil(ceil(ceil(K/128)/4) / (k_steps_per_wave/4)) workgroups cover K,
+ * their fp32 partials summed by the reduce kernel (split_reduce must be
+ * MXFP4_REDUCE_KERNEL).  waves_n must be 4 and waves_k 1.  Same products
+ * as the other modes with the 16x16x128 instruction; the sums differ only
+ * in order.  K must be <= 4194304 (2^22).
  * ---------------------------------------------------------------------- */
 #define MXFP4_MODE_FUSED 1
 #define MXFP4_MODE_PREQUANT 2
 #define MXFP4_MODE_TILED 3
+#define MXFP4_MODE_STREAM 4
 
 #define MXFP4_REDUCE_KERNEL 0
 #define MXFP4_REDUCE_LAST_WG 1
 #define MXFP4_REDUCE_ATOMIC 2
 
 typedef struct mxfp4_plan {
-    int mode;             /* MXFP4_MODE_FUSED, _PREQUANT or _TILED */
+    int mode;             /* MXFP4_MODE_FUSED, _PREQUANT, _TILED or _STREAM */
     int m_blocks;         /* 16-row blocks of A per workgroup: 1, 2 or 4 */
     int n_tiles_per_wave; /* 16-column tiles of B per wavefront: 1 or 2 */
     int waves_n;          /* wavefronts along N per workgroup */

@@ -120,6 +120,44 @@ def test_plan_checks(lib):
                  m=1 << 17, n=1 << 17, k=256) == 0
 
 
+def test_stream_plan(lib):
+    """Stream-mode plan rules: four wavefronts along N, one along K, the
+    workgroup's K steps a multiple of 4, split_k the workgroups that cover K
+    with them, the reduce kernel for the split; and the default plan takes the
+    mode for long K and a large B below M = 256 only."""
+    def check(p, M, N, K):
+        return lib.mxfp4_check_plan(ctypes.byref(p._c()), M, N, K)
+    S = mx.MODE_STREAM
+    M, N, K = 64, 1024, 16384  # 128 steps, 32 chunks
+    assert check(mx.Plan(S, 4, 1, 4, 1, 128, 1, 0), M, N, K) == 0
+    assert check(mx.Plan(S, 4, 2, 4, 1, 32, 4, 0), M, N, K) == 0
+    assert check(mx.Plan(S, 2, 1, 4, 1, 12, 11, 0), M, N, K) == 0     # 3 chunks per workgroup: 11 workgroups
+    assert check(mx.Plan(S, 2, 1, 4, 1, 12, 3, 0), M, N, K) == EINVAL
+    assert check(mx.Plan(S, 4, 1, 8, 1, 128, 1, 0), M, N, K) == EINVAL  # waves_n
+    assert check(mx.Plan(S, 4, 1, 4, 2, 128, 1, 0), M, N, K) == EINVAL  # waves_k
+    assert check(mx.Plan(S, 4, 1, 4, 1, 126, 1, 0), M, N, K) == EINVAL  # not whole chunks
+    assert check(mx.Plan(S, 4, 1, 4, 1, 132, 1, 0), M, N, K) == EINVAL  # past K
+    assert check(mx.Plan(S, 4, 1, 4, 1, 32, 3, 0), M, N, K) == EINVAL   # covers 96 of 128 steps
+    assert check(mx.Plan(S, 4, 1, 4, 1, 32, 4, 1), M, N, K) == EINVAL   # last-workgroup reduce
+    assert check(mx.Plan(S, 3, 1, 4, 1, 128, 1, 0), M, N, K) == ENOTSUP  # m_blocks
+    assert check(mx.Plan(S, 4, 1, 4, 1, 4, 1 << 20, 0), 1, 1, 1 << 23) == EINVAL  # K > 2^22
+    assert check(mx.Plan(S, 1, 1, 4, 1, 1 << 30, 1, 0), M, N, K) == EINVAL
+    # workspace: MX-packed A, then split partials
+    ws = mx.workspace_bytes(M, N, K, mx.Plan(S, 4, 1, 4, 1, 32, 4, 0))
+    a = mx.packed_bytes(M, K)
+    assert ws == -(-a // 256) * 256 + 4 * M * N * 4
+    assert mx.prequant_workspace_bytes(M, N, K, mx.Plan(S, 4, 1, 4, 1, 32, 4, 0)) == 4 * M * N * 4
+    # the default plan
+    for shape in [(64, 16384, 16384), (32, 16384, 4096), (128, 8192, 8192), (96, 4096, 14336),
+                  (32, 8192, 28672), (255, 16384, 16384)]:
+        p = mx.default_plan(*shape)
+        assert p.mode == S, (shape, p)
+        mx.check_plan(p, *shape)
+    for shape in [(16, 16384, 16384), (32, 8192, 8192), (96, 4096, 4096), (256, 16384, 16384),
+                  (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048)]:
+        assert mx.default_plan(*shape).mode != S, shape
+
+
 def test_tiled_plan(lib):
     # the tiled mode has a fixed tiling: the other fields are not checked
     M, N, K = 300, 520, 640
@@ -248,7 +286,10 @@ def test_default_plans_valid_on_random_shapes(lib):
     for M, N, K in shapes:
         p = mx.default_plan(M, N, K)
         mx.check_plan(p, M, N, K)
-        if p.mode != mx.MODE_TILED:  # the tiled mode's tiling is fixed
+        if p.mode == mx.MODE_STREAM:  # whole chunks of four steps per workgroup
+            kg = -(-(-(-K // 128)) // 4)
+            assert p.k_steps_per_wave % 4 == 0 and p.split_k == -(-kg // (p.k_steps_per_wave // 4)), (M, N, K, p)
+        elif p.mode != mx.MODE_TILED:  # the tiled mode's tiling is fixed
             assert p.split_k * p.waves_k * p.k_steps_per_wave == -(-K // 128), (M, N, K, p)
         assert mx.workspace_bytes(M, N, K) == mx.workspace_bytes(M, N, K, p)
         assert mx.default_plan(M, N, K) == p  # cached pick is the same

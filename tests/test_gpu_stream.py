@@ -61,3 +61,74 @@ def test_stream_shape_sampled(case):
     assert not torch.isnan(c).any().item()
     del c, b_packed, dev_a
     torch.cuda.empty_cache()
+
+
+S = mx.MODE_STREAM
+
+
+def stream_plan(mbw, ntw, steps, M, N, K):
+    """A stream-mode plan with `steps` 128-K steps per workgroup."""
+    kg = -(-(-(-K // 128)) // 4)
+    return mx.Plan(S, mbw, ntw, 4, 1, steps, -(-kg // (steps // 4)), 0)
+
+
+# shapes the oracle finishes in seconds: ragged M (across row blocks and
+# row groups), ragged N, K not a multiple of 128 or of 512, one chunk and
+# many, one workgroup along K and several
+SMALL = [
+    (1, 200, 512, 1, 1, 4),       # one chunk per workgroup, split 1
+    (16, 1040, 2080, 1, 2, 8),    # K = 16.25 steps (17 steps, 5 chunks): split 3, last chunk partial
+    (37, 264, 4096, 4, 1, 32),    # M across three row blocks, whole K in one workgroup
+    (37, 264, 4096, 2, 2, 12),    # two row groups, split 3
+    (64, 520, 8192, 4, 2, 64),    # whole K (64 steps) in one workgroup
+    (100, 320, 1536, 4, 1, 4),    # two row groups, 12 steps: split 3
+    (3, 4096, 640, 1, 2, 8),      # 5 steps: one chunk of four and a partial one
+]
+
+
+@pytest.mark.parametrize("M,N,K,mbw,ntw,steps", SMALL)
+def test_stream_mode_against_oracle(M, N, K, mbw, ntw, steps):
+    plan = stream_plan(mbw, ntw, steps, M, N, K)
+    print("case stream mode", M, N, K, plan, flush=True)
+    mx.check_plan(plan, M, N, K)
+    a, b = inputs.make_shape(M, N, K, seed=M * 13 + N + K)
+    ref = oracle.reference(a, b)
+    bq, bs = oracle.quantize(b)
+    from gpu_util import to_dev_u8
+    b_packed = mx.pack_b(to_dev_u8(bq), to_dev_u8(bs))
+    dev_a = to_dev_bf16(a)
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev_a.device)
+    mx.gemm(dev_a, b_packed, N, out=c, plan=plan)
+    # the same plan on an A quantized beforehand (the prequant entry point)
+    c2 = mx.gemm_prequant(mx.quant_a_packed(dev_a), M, b_packed, N, K, plan=plan)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bf16_out_to_f32(c), ref["c32"], "stream %dx%dx%d" % (M, N, K))
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,mbw,ntw,steps", [(64, 16384, 16384, 4, 1, 128),
+                                                 (16, 8192, 28672, 1, 1, 32),
+                                                 (32, 28672, 8192, 2, 2, 64)])
+def test_stream_mode_large_sampled(M, N, K, mbw, ntw, steps):
+    plan = stream_plan(mbw, ntw, steps, M, N, K)
+    print("case stream mode large", M, N, K, plan, flush=True)
+    a, b = inputs.make_shape(M, N, K, seed=(M + N + K) % 991)
+    dev_a = to_dev_bf16(a)
+    dev_b = to_dev_bf16(b)
+    bq, bs = mx.quant_a(dev_b)
+    del dev_b
+    b_packed = mx.pack_b(bq, bs)
+    del bq, bs
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev_a.device)
+    mx.gemm(dev_a, b_packed, N, out=c, plan=plan)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M * 5 + N)
+    cols = np.unique(np.concatenate([[0, N - 1, N // 2, 63, 64], rng.integers(0, N, 59)]))
+    aq, asc = oracle.quantize(a)
+    bq_h, bs_h = oracle.quantize(b[cols])
+    want, _ = oracle.gemm(oracle.dequantize(aq, asc), oracle.dequantize(bq_h, bs_h), want64=False)
+    got = bf16_out_to_f32(c[:, torch.as_tensor(cols, device=c.device)])
+    assert_close_to_oracle(got, want, "stream mode %dx%dx%d sampled" % (M, N, K))
+    assert not torch.isnan(c).any().item()
+    del c, b_packed, dev_a
+    torch.cuda.empty_cache()

@@ -29,6 +29,7 @@ CASES = [
     (64, 7168, 2048, 2056, 7171, mx.Plan(F, 4, 1, 2, 1, 4, 4, mx.REDUCE_ATOMIC)),
     (37, 1000, 1504, 1512, 1003, mx.Plan(F, 2, 1, 2, 3, 4, 1)),           # ragged M, N, K
     (256, 3072, 1536, 1544, 3080, mx.Plan(P, 2, 1, 6, 1, 12, 1)),         # pre-quantized A
+    (40, 520, 4096, 4104, 523, mx.Plan(mx.MODE_STREAM, 4, 1, 4, 1, 16, 2, 0)),  # stream, split 2
     (16, 2112, 7168, 7200, 2115, NOALLOC),                                 # allocation-free entry
 ]
 

@@ -19,12 +19,14 @@ from gpu_util import to_dev_bf16  # noqa: E402
 # scratch for split-K partials (16x2112x7168: 946,176 bytes; 8x2112x7168:
 # 473,088), for the pre-quantized A of the tiled kernel (1024x4096x4096:
 # 2,228,224; 512x4096x4096: 1,114,112) and of the pre-quantized plan
-# (768x2048x2048: 835,584; 600x3072x2048: 661,504), or not at all
-# (64x7168x2048, 4x2880x512).
+# (768x2048x2048: 835,584; 600x3072x2048: 661,504), for the pre-quantized A
+# and the split partials of the stream kernel (32x8192x28672: 2,584,576;
+# 96x8192x8192: 417,792, no split), or not at all (64x7168x2048, 4x2880x512).
 PAIRS = [
     ((16, 2112, 7168), (8, 2112, 7168)),
     ((1024, 4096, 4096), (512, 4096, 4096)),
     ((768, 2048, 2048), (600, 3072, 2048)),
+    ((32, 8192, 28672), (96, 8192, 8192)),
     ((64, 7168, 2048), (4, 2880, 512)),
 ]
 
