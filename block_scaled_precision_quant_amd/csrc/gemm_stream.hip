@@ -39,7 +39,6 @@ struct StreamArgs {
   int chunks;         // chunks per workgroup (the last workgroup's range may end past K)
 };
 
-// LDS bytes of one stage: A data, B data, A scale dwords, B scale dwords.
 // B's copies carry the nontemporal hint: each B byte is read once per row
 // group and streams through the caches (at 16x16384x16384, 38 us per call
 // against 60 us with plain copies; A, which every column group re-reads,
@@ -48,6 +47,7 @@ __device__ inline void dma16_stream(BufRsrc r, uint8_t* lds, int voff, int soff)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, kCachePolicyNT);
 }
 
+// LDS bytes of one stage: A data, B data, A scale dwords, B scale dwords.
 template <int MBW, int NTW>
 struct StreamStage {
   static constexpr int a_data = 0;
@@ -162,11 +162,6 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
 #pragma unroll
     for (int i = 0; i < NTW; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Products of chunk c from stage `stage`.  Steps past K, and every step
-  // of chunks past the workgroup's range (copied only to keep the count of
-  // copies in flight fixed), take scale byte 0 for both operands: a product
-  // of at most 36 * 2^-254, which leaves every fp32 sum unchanged.  No
-  // branch: the loop body stays one straight block per stage.
   // Per-lane read offsets inside a stage, each one value (the reads' address
   // chains stay short and separate from the copies' destinations, so the
   // compiler keeps the stage of every read and waits only for that stage's
@@ -175,6 +170,11 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
   const int rd_b = lane * 16 + wave * (NTW * kSCh * kBlockBytes);
   const int rd_as = lane * 4;
   const int rd_bs = lane * 4 + wave * (NTW * 256);
+  // Products of chunk c from stage `stage`.  Steps past K, and every step
+  // of chunks past the workgroup's range (copied only to keep the count of
+  // copies in flight fixed), take scale byte 0 for both operands: a product
+  // of at most 36 * 2^-254, which leaves every fp32 sum unchanged.  No
+  // branch: the loop body stays one straight block per stage.
   auto multiply = [&](int c, const uint8_t* stage) {
     const int step0 = (chunk0 + c) * kSCh;
     const uint32_t live = c < nch ? 0xFFu : 0u;

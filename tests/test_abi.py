@@ -158,6 +158,17 @@ def test_stream_plan(lib):
         assert mx.default_plan(*shape).mode != S, shape
 
 
+def test_small_m_rule(lib):
+    """Up to 16 rows against a large B with long K, the default plan is the
+    fused kernel with eight wavefronts along N and K split over workgroups."""
+    for M, N, K in [(1, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672), (2, 16384, 8192)]:
+        p = mx.default_plan(M, N, K)
+        assert (p.mode, p.m_blocks, p.waves_n, p.waves_k) == (mx.MODE_FUSED, 1, 8, 1), (M, N, K, p)
+        assert p.k_steps_per_wave in (16, 14, 12, 8) and p.split_reduce == mx.REDUCE_KERNEL
+        assert p.split_k * p.k_steps_per_wave == -(-K // 128)
+        mx.check_plan(p, M, N, K)
+
+
 def test_tiled_plan(lib):
     # the tiled mode has a fixed tiling: the other fields are not checked
     M, N, K = 300, 520, 640
