@@ -358,16 +358,17 @@ mxfp4_plan cached_model_plan(int M, int N, int K) {
   return p;
 }
 
-// Stream mode for long K and a large B below M = 256 (a rule measured
-// L2-cold against the cost model's pick on 91 shapes, M 1..256, N x K 17M ..
-// 268M: it is taken where the stream kernel was faster on every measured
+// Stream mode for long K and a large B with 17 <= M <= 255 (a rule measured
+// L2-cold against the cost model's pick on 111 shapes, M 1..256, N x K 17M
+// .. 268M: it is taken where the stream kernel was faster on every measured
 // shape of its class -- 1.1-1.9x with M >= 96 and N x K >= 55M, 1.05-1.5x
-// with M >= 32 and either N >= 16384 or N x K >= 200M -- and left out where
-// it lost, below those sizes or with M < 32).
+// with M >= 32 and N >= 16384, 1.04-1.2x with M >= 17, K >= 8192 and N x K
+// >= 100M -- and left out where it lost: M <= 16, or below those sizes).
 bool use_stream(int M, int N, int K) {
   const long long nk = (long long)N * K;
   if (M > 255 || K < 4096 || nk < 55LL * 1000 * 1000) return false;
-  return M >= 96 || (M >= 32 && (N >= 16384 || nk >= 200LL * 1000 * 1000));
+  if (M >= 96 || (M >= 32 && N >= 16384)) return true;
+  return M >= 17 && K >= 8192 && nk >= 100LL * 1000 * 1000;
 }
 
 // The stream plan: every row block of up to 64 rows in one workgroup (one

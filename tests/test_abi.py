@@ -124,7 +124,7 @@ def test_stream_plan(lib):
     """Stream-mode plan rules: four wavefronts along N, one along K, the
     workgroup's K steps a multiple of 4, split_k the workgroups that cover K
     with them, the reduce kernel for the split; and the default plan takes the
-    mode for long K and a large B below M = 256 only."""
+    mode for long K and a large B with 17 <= M <= 255 only."""
     def check(p, M, N, K):
         return lib.mxfp4_check_plan(ctypes.byref(p._c()), M, N, K)
     S = mx.MODE_STREAM
@@ -149,12 +149,12 @@ def test_stream_plan(lib):
     assert mx.prequant_workspace_bytes(M, N, K, mx.Plan(S, 4, 1, 4, 1, 32, 4, 0)) == 4 * M * N * 4
     # the default plan
     for shape in [(64, 16384, 16384), (32, 16384, 4096), (128, 8192, 8192), (96, 4096, 14336),
-                  (32, 8192, 28672), (255, 16384, 16384)]:
+                  (32, 8192, 28672), (255, 16384, 16384), (20, 12288, 12288), (17, 16384, 8192)]:
         p = mx.default_plan(*shape)
         assert p.mode == S, (shape, p)
         mx.check_plan(p, *shape)
     for shape in [(16, 16384, 16384), (32, 8192, 8192), (96, 4096, 4096), (256, 16384, 16384),
-                  (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048)]:
+                  (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048), (24, 16384, 4096)]:
         assert mx.default_plan(*shape).mode != S, shape
 
 
