@@ -358,45 +358,81 @@ mxfp4_plan cached_model_plan(int M, int N, int K) {
   return p;
 }
 
-// Stream mode for long K and a large B with 17 <= M <= 255 (a rule measured
-// L2-cold against the cost model's pick on 111 shapes, M 1..256, N x K 17M
-// .. 268M: it is taken where the stream kernel was faster on every measured
-// shape of its class -- 1.1-1.9x with M >= 96 and N x K >= 55M, 1.05-1.5x
-// with M >= 32 and N >= 16384, 1.04-1.2x with M >= 17, K >= 8192 and N x K
-// >= 100M -- and left out where it lost: M <= 16, or below those sizes).
-bool use_stream(int M, int N, int K) {
-  const long long nk = (long long)N * K;
-  if (M > 255 || K < 4096 || nk < 55LL * 1000 * 1000) return false;
-  if (M >= 96 || (M >= 32 && N >= 16384)) return true;
-  return M >= 17 && K >= 8192 && nk >= 100LL * 1000 * 1000;
-}
-
-// The stream plan: every row block of up to 64 rows in one workgroup (one
-// block or two for M <= 32), 16-column tiles per wavefront (two for 65..128
-// rows and N >= 16384, where that measured faster), and the smallest split
-// of K that gives 192 workgroups or more.
-mxfp4_plan stream_plan(int M, int N, int K) {
-  const int MT = (M + 15) / 16, KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
-  const long long NT = ((long long)N + 15) / 16;
-  const int mbw = MT <= 2 ? MT : 4;
-  const int ntw = (MT >= 5 && MT <= 8 && N >= 16384) ? 2 : 1;
+// Smallest split of K over workgroups that gives the stream kernel 192
+// workgroups or more (all of K when fewer chunks are left).
+int stream_split(int M, int N, int K, int mbw, int ntw) {
+  const long long MT = ((long long)M + 15) / 16, NT = ((long long)N + 15) / 16;
+  const int KG = (int)((((long long)K + 127) / 128 + 3) / 4);
   const long long mg = (MT + mbw - 1) / mbw, ng = (NT + 4 * ntw - 1) / (4 * ntw);
   int split = 1;
   while (ng * mg * split < 192 && split < KG) ++split;
+  return split;
+}
+
+// The stream plan: the row blocks of up to 64 rows in one workgroup (one
+// block or two for M <= 32), fewer (halving) while that would need K split
+// over workgroups and K < 20480 (a split adds the reduce launch and fp32
+// partials, which only a long K repays), two 16-column tiles per wavefront
+// with 65 rows or more, four row blocks, N x K >= 50M and no split, and the
+// smallest split that gives 192 workgroups.  On the 225 training shapes of
+// the rule below this pick was a mean 0.3 % (at most 6 %) slower than the
+// fastest of the six tilings with one, two or four row blocks and one or two
+// tiles per wavefront; on ten held-out shapes where only the tiles per
+// wavefront differ from the previous rule's pick, 0.90-1.06 of its time.
+mxfp4_plan stream_plan(int M, int N, int K) {
+  const int MT = (M + 15) / 16, KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
+  int mbw = MT <= 2 ? MT : 4;
+  while (mbw > 1 && K < 20480 && stream_split(M, N, K, mbw, 1) > 1) mbw /= 2;
+  const int ntw = (MT >= 5 && mbw == 4 && (long long)N * K >= 50LL * 1000 * 1000 &&
+                   stream_split(M, N, K, 4, 2) == 1)
+                      ? 2
+                      : 1;
+  const int split = stream_split(M, N, K, mbw, ntw);
   const int chunks = (KG + split - 1) / split;
   return make_plan(MXFP4_MODE_STREAM, mbw, ntw, 4, 1, 4 * chunks, (KG + chunks - 1) / chunks);
 }
 
-// One row block (M <= 16) against a large B with long K: the fused kernel
-// with eight wavefronts along N, 16 (or 14, 12, 8) steps per wavefront and K
-// split over workgroups.  A rule measured L2-cold against the cost model's
-// pick on 54 shapes (M 1..16, N x K 59M..268M): with K >= 8192 and N x K
-// >= 100M it was 1.01-1.31x as fast on 28 of the 30 shapes (0.99x on the
-// other two); below those sizes it lost by up to 12 %.
+// Stream mode where it measured faster.  Rules fitted on 225 training shapes
+// (M 1..255 against 15 sizes of B, N x K 17M..268M, K >= 4096), timed
+// L2-cold against the cost model's or the small-M rule's pick, then checked
+// on two sets of 110 held-out shapes (M 3..250, twenty other sizes of B).
+// Time of the stream plan over the other pick on the training shapes: with
+// M >= 96, 0.58-0.94 (20 shapes); with M 17..95 where its workgroups keep
+// two or four row blocks and N >= 4096 (M >= 48), N >= 7168, or K >= 8192
+// and N x K >= 100M, 0.65-0.94 (29); with M <= 16 against a large B with
+// long K and no split of K unless K >= 20480, 0.88-1.00 (13).  Left out:
+// one row block below M = 96 (B is read once per 16 rows; 1.06-1.09 on
+// four held-out shapes), a split with K < 20480 at M <= 16 (1.20 at
+// 14x8192x16384), and smaller B at M <= 16 (up to 1.46).
+bool use_stream(int M, int N, int K) {
+  const long long nk = (long long)N * K;
+  if (M > 255 || K < 4096 || nk < 16LL * 1000 * 1000) return false;
+  const mxfp4_plan p = stream_plan(M, N, K);
+  if (M <= 16)
+    return K >= 8192 && (p.split_k == 1 || K >= 20480) &&
+           ((nk >= 150LL * 1000 * 1000 && M >= 8) || (nk >= 100LL * 1000 * 1000 && M >= 13));
+  if (M >= 96) return N >= 2048;
+  if (p.m_blocks == 1) return false;
+  if (K >= 8192 && nk >= 100LL * 1000 * 1000) return true;
+  return N >= (M >= 48 ? 4096 : 7168);
+}
+
+// Small M against a B with long K: the fused kernel with one row block and
+// eight wavefronts along N, 16 (or 14, 12, 8) steps per wavefront and K
+// split over workgroups.  Measured L2-cold against the cost model's pick: on
+// 54 shapes with M 1..16 and N x K 59M..268M, 1.01-1.31x as fast on 28 of
+// the 30 shapes with K >= 8192 and N x K >= 100M (0.99x on two), losing by
+// up to 12 % below those sizes; on the 225 shapes of the stream rule, where
+// that rule leaves M <= 32 with N <= 4096, 1.03-1.13x as fast with M 17..32,
+// K >= 8192 and N x K >= 30M, and 1.00-1.14x with M <= 16 and K >= 14336
+// (0.996x on one of 18), but 0.93-0.98x with M <= 16 and K = 8192.
 mxfp4_plan small_m_plan(int M, int N, int K, bool* ok) {
   const int KS = (int)(((long long)K + 127) / 128);
+  const long long nk = (long long)N * K;
   *ok = false;
-  if (M > 16 || K < 8192 || (long long)N * K < 100LL * 1000 * 1000) return mxfp4_plan{};
+  const bool take = M <= 16 ? K >= 8192 && (nk >= 100LL * 1000 * 1000 || (K >= 14336 && nk >= 30LL * 1000 * 1000))
+                            : M <= 32 && N <= 4096 && K >= 8192 && nk >= 30LL * 1000 * 1000;
+  if (!take) return mxfp4_plan{};
   for (int ksw : {16, 14, 12, 8})
     if (KS % ksw == 0) {
       *ok = true;

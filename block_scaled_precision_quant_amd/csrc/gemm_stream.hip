@@ -5,19 +5,21 @@
 // against 4 x NTW 16-column tiles of B (one group of NTW tiles per
 // wavefront) over a range of K that may be as long as the whole of K.  K
 // advances one chunk of four 128-K steps at a time (one scale dword per
-// lane): every operand byte of a chunk -- the MBW x 4 A blocks and A scale
-// dwords, each wavefront's NTW x 4 B blocks and B scale dwords -- is moved
-// into one stage of a three-stage LDS ring by direct global-to-LDS copies,
-// issued two chunks ahead of its use, and every wavefront issues the same
-// number of copies per chunk, so one wait on the vector-memory counter
-// finds a chunk complete while the two after it stay in flight.  The
-// products are the 16x16x128 block-scaled FP4 instruction of the other
-// GEMM kernel, with the same lane map and the same per-lane scale bytes.
+// lane).  A chunk's MBW x 4 A blocks and A scale dwords, which all four
+// wavefronts multiply, are moved into one stage of a four-stage LDS ring by
+// direct global-to-LDS copies; each wavefront's own NTW x 4 B blocks and B
+// scale dwords, used by that wavefront alone, are loaded straight into its
+// registers (a ring of four register sets).  Both are issued three chunks
+// ahead of their use, and every wavefront issues the same number of
+// vector-memory instructions per chunk, so one wait on that counter finds a
+// chunk complete while the three after it stay in flight.  The products
+// are the 16x16x128 block-scaled FP4 instruction of the other GEMM kernel,
+// with the same lane map and the same per-lane scale bytes.
 //
 // Rows past M take scale byte 0 and are never stored; row and column tiles
 // past the matrices read the last tile instead and are never stored; steps
-// past K are copied from the last step and multiplied with scale byte 0 on
-// both operands, which adds nothing.  With split > 1 each
+// past K read the last step and are multiplied with scale byte 0 on both
+// operands, which adds nothing.  With split > 1 each
 // workgroup writes an fp32 partial [split][M][N], summed by the reduce
 // kernel of gemm.hip.
 #include "mx_internal.hpp"
@@ -26,7 +28,7 @@ namespace mx {
 
 constexpr int kSWaves = 4;      // wavefronts per workgroup, all along N
 constexpr int kSCh = 4;         // 128-K steps per chunk (one scale dword)
-constexpr int kSStages = 3;     // LDS ring: the chunk being multiplied + two in flight
+constexpr int kSStages = 4;     // ring depth: the chunk being multiplied + three in flight
 
 struct StreamArgs {
   const uint8_t* ap;  // MX-packed A (MT row tiles)
@@ -39,47 +41,55 @@ struct StreamArgs {
   int chunks;         // chunks per workgroup (the last workgroup's range may end past K)
 };
 
-// B's copies carry the nontemporal hint: each B byte is read once per row
+// B's loads carry the nontemporal hint: each B byte is read once per row
 // group and streams through the caches (at 16x16384x16384, 38 us per call
-// against 60 us with plain copies; A, which every column group re-reads,
-// keeps plain ones).
-__device__ inline void dma16_stream(BufRsrc r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, kCachePolicyNT);
+// against 60 us without it; A, which every column group re-reads, keeps
+// plain copies).  B goes to registers, not through LDS: each B block feeds
+// one wavefront only, and the copy engine's path into LDS moved fewer bytes
+// per second than plain loads (the kernel with B staged in LDS took 5-15 %
+// longer per call on the weight-streaming shapes).
+__device__ inline uint4 ld16_stream(BufRsrc r, int voff, int soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ inline uint32_t ld4_stream(BufRsrc r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCachePolicyNT);
 }
 
-// LDS bytes of one stage: A data, B data, A scale dwords, B scale dwords.
+// LDS bytes of one stage: A data, then A scale dwords.
 template <int MBW, int NTW>
 struct StreamStage {
   static constexpr int a_data = 0;
-  static constexpr int b_data = MBW * kSCh * kBlockBytes;
-  static constexpr int a_scale = b_data + kSWaves * NTW * kSCh * kBlockBytes;
-  static constexpr int b_scale = a_scale + MBW * 256;
-  static constexpr int bytes = b_scale + kSWaves * NTW * 256;
-  // copy instructions each wavefront issues per chunk: MBW A blocks (the
-  // workgroup's MBW*4 split four ways), one A scale block (wavefront w takes
-  // block w % MBW; with MBW < 4 several wavefronts copy the same bytes to the
-  // same place), and its own NTW*4 B blocks and NTW B scale blocks
+  static constexpr int a_scale = MBW * kSCh * kBlockBytes;
+  static constexpr int bytes = a_scale + MBW * 256;
+  // vector-memory instructions each wavefront issues per chunk: MBW A block
+  // copies (the workgroup's MBW*4 split four ways), one A scale block copy
+  // (wavefront w takes block w % MBW; with MBW < 4 several wavefronts copy
+  // the same bytes to the same place), and the loads of its own NTW*4 B
+  // blocks and NTW B scale blocks
   static constexpr int copies = MBW + 1 + 5 * NTW;
 };
 
 // Waits until at most N of this wavefront's vector-memory instructions are
 // outstanding and its LDS accesses are done, then the workgroup barrier.
-// An asm statement: the compiler's barrier would wait for every copy.
+// An asm statement: the compiler's barrier would wait for every copy.  (The
+// compiler adds its own waits before the uses of the B registers; they ask
+// for no more than this one has already ensured.)
 template <int N>
 __device__ inline void stream_wait_barrier() {
 #define MX_STREAM_WAIT(n) \
   if constexpr (N == n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  MX_STREAM_WAIT(7)
-  MX_STREAM_WAIT(8)
-  MX_STREAM_WAIT(10)
-  MX_STREAM_WAIT(12)
-  MX_STREAM_WAIT(13)
-  MX_STREAM_WAIT(15)
+  MX_STREAM_WAIT(14)
+  MX_STREAM_WAIT(16)
+  MX_STREAM_WAIT(20)
+  MX_STREAM_WAIT(24)
+  MX_STREAM_WAIT(26)
+  MX_STREAM_WAIT(30)
 #undef MX_STREAM_WAIT
-  static_assert(N == 7 || N == 8 || N == 10 || N == 12 || N == 13 || N == 15, "copy counts of the tilings");
+  static_assert(N == 14 || N == 16 || N == 20 || N == 24 || N == 26 || N == 30, "copy counts of the tilings");
 }
 
-// The three stages as separate arrays: the compiler tracks the copies into
+// The four stages as separate arrays: the compiler tracks the copies into
 // each on its own, so a read of one stage waits only for the copies into it.
 template <int MBW, int NTW>
 __shared__ __align__(16) uint8_t g_sring0[StreamStage<MBW, NTW>::bytes];
@@ -87,6 +97,8 @@ template <int MBW, int NTW>
 __shared__ __align__(16) uint8_t g_sring1[StreamStage<MBW, NTW>::bytes];
 template <int MBW, int NTW>
 __shared__ __align__(16) uint8_t g_sring2[StreamStage<MBW, NTW>::bytes];
+template <int MBW, int NTW>
+__shared__ __align__(16) uint8_t g_sring3[StreamStage<MBW, NTW>::bytes];
 
 template <int MBW, int NTW>
 __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g) {
@@ -125,19 +137,24 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
   const BufRsrc rbs = make_rsrc(g.bp + db.data_bytes() + (size_t)t_b0 * g.KG * 256, b_tiles * g.KG * 256);
   const int lane16 = lane * 16, lane4 = lane * 4;
 
-  // Issue every copy of chunk c (0-based within the workgroup) into stage st.
-  auto issue = [&](int c, uint8_t* stage) {
+  // Issue chunk c (0-based within the workgroup): A's copies into LDS stage
+  // `stage`, B's loads into the register set bv, bsv.  A chunk past the
+  // workgroup's range (issued only to keep the count in flight fixed) reads
+  // the same valid 16 (or 4) bytes on every lane: one cache line instead of
+  // a chunk of the operands.
+  auto issue = [&](int c, uint8_t* stage, uint4 (&bv)[NTW][kSCh], uint32_t (&bsv)[NTW]) {
     const int cg = chunk0 + c;
+    const int v16 = c < nch ? lane16 : 0, v4 = c < nch ? lane4 : 0;
 #pragma unroll
     for (int i = 0; i < MBW; ++i) {  // A blocks q = wave + 4 i of MBW x 4: block i, step wave
       const int q = wave + kSWaves * i;
       const int b = min(q / kSCh, a_tiles - 1), j = q % kSCh;
       const int step = min(cg * kSCh + j, g.KS - 1);
-      dma16(ra, stage + St::a_data + q * kBlockBytes, lane16, (b * g.KS + step) * kBlockBytes);
+      dma16(ra, stage + St::a_data + q * kBlockBytes, v16, (b * g.KS + step) * kBlockBytes);
     }
     {
       const int b = min(wave % MBW, a_tiles - 1);
-      dma4(ras, stage + St::a_scale + (wave % MBW) * 256, lane4, (b * g.KG + min(cg, g.KG - 1)) * 256);
+      dma4(ras, stage + St::a_scale + (wave % MBW) * 256, v4, (b * g.KG + min(cg, g.KG - 1)) * 256);
     }
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
@@ -146,10 +163,9 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
 #pragma unroll
       for (int j = 0; j < kSCh; ++j) {
         const int step = min(cg * kSCh + j, g.KS - 1);
-        dma16_stream(rb, stage + St::b_data + (slot_b * kSCh + j) * kBlockBytes, lane16,
-                     (lb * g.KS + step) * kBlockBytes);
+        bv[i][j] = ld16_stream(rb, v16, (lb * g.KS + step) * kBlockBytes);
       }
-      dma4(rbs, stage + St::b_scale + slot_b * 256, lane4, (lb * g.KG + min(cg, g.KG - 1)) * 256);
+      bsv[i] = ld4_stream(rbs, v4, (lb * g.KG + min(cg, g.KG - 1)) * 256);
     }
   };
 
@@ -167,15 +183,13 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
   // compiler keeps the stage of every read and waits only for that stage's
   // copies).
   const int rd_a = lane * 16;
-  const int rd_b = lane * 16 + wave * (NTW * kSCh * kBlockBytes);
   const int rd_as = lane * 4;
-  const int rd_bs = lane * 4 + wave * (NTW * 256);
-  // Products of chunk c from stage `stage`.  Steps past K, and every step
-  // of chunks past the workgroup's range (copied only to keep the count of
-  // copies in flight fixed), take scale byte 0 for both operands: a product
-  // of at most 36 * 2^-254, which leaves every fp32 sum unchanged.  No
-  // branch: the loop body stays one straight block per stage.
-  auto multiply = [&](int c, const uint8_t* stage) {
+  // Products of chunk c from LDS stage `stage` and registers bvr, bsr.
+  // Steps past K, and every step of chunks past the workgroup's range, take
+  // scale byte 0 for both operands: a product of at most 36 * 2^-254, which
+  // leaves every fp32 sum unchanged.  No branch: the loop body stays one
+  // straight block per stage.
+  auto multiply = [&](int c, const uint8_t* stage, const uint4 (&bvr)[NTW][kSCh], const uint32_t (&bsr)[NTW]) {
     const int step0 = (chunk0 + c) * kSCh;
     const uint32_t live = c < nch ? 0xFFu : 0u;
     uint32_t as[MBW], bs[NTW];
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
       as[b] = *reinterpret_cast<const uint32_t*>(stage + (rd_as + St::a_scale + b * 256));
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
-      bs[i] = *reinterpret_cast<const uint32_t*>(stage + (rd_bs + St::b_scale + i * 256));
+      bs[i] = bsr[i];
 #pragma unroll
     for (int j = 0; j < kSCh; ++j) {
       const uint32_t ok = step0 + j < g.KS ? live : 0u;
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
         av[b] = *reinterpret_cast<const uint4*>(stage + (rd_a + St::a_data + (b * kSCh + j) * kBlockBytes));
 #pragma unroll
       for (int i = 0; i < NTW; ++i)
-        bv[i] = *reinterpret_cast<const uint4*>(stage + (rd_b + St::b_data + (i * kSCh + j) * kBlockBytes));
+        bv[i] = bvr[i][j];
 #pragma unroll
       for (int b = 0; b < MBW; ++b) {
         const int asc = (int)((as[b] >> (8 * j)) & rowmask[b] & ok);
@@ -205,27 +219,38 @@ __global__ __launch_bounds__(kSWaves * 64) void gemm_stream_kernel(StreamArgs g)
     }
   };
 
-  // Chunk c's copies are issued two loop steps before its products, into
-  // stage c % 3, unconditionally: chunks past the workgroup's range copy
-  // clamped (valid) addresses and are never multiplied, so every step has
-  // the same copies in flight and one count waits for exactly chunk c.  The
-  // loop runs a multiple of three steps with the stages named in each.
+  // Chunk c is issued three loop steps before its products, into stage and
+  // register set c % 4, unconditionally (chunks past the workgroup's range
+  // are never multiplied), so every step has the same instructions in flight
+  // and one count waits for exactly chunk c.  The loop runs a multiple of
+  // four steps with the stages and register sets named in each.  The
+  // scheduling barriers keep the prologue's three chunks in issue order, so
+  // the compiler's own count of the loads in flight at the loop head is
+  // exact and its waits before B's uses never hold a later chunk.
   constexpr int kC = St::copies;
   uint8_t* const ring0 = g_sring0<MBW, NTW>;
   uint8_t* const ring1 = g_sring1<MBW, NTW>;
   uint8_t* const ring2 = g_sring2<MBW, NTW>;
-  issue(0, ring0);
-  issue(1, ring1);
+  uint8_t* const ring3 = g_sring3<MBW, NTW>;
+  uint4 b0[NTW][kSCh], b1[NTW][kSCh], b2[NTW][kSCh], b3[NTW][kSCh];
+  uint32_t s0[NTW], s1[NTW], s2[NTW], s3[NTW];
+  issue(0, ring0, b0, s0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, ring1, b1, s1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(2, ring2, b2, s2);
+  __builtin_amdgcn_sched_barrier(0);
   const int nloop = (nch + kSStages - 1) / kSStages * kSStages;
-#define MX_STREAM_STEP(R, R2)          \
-  stream_wait_barrier<kC>();           \
-  issue(c + 2, R2);                    \
-  multiply(c, R);                      \
+#define MX_STREAM_STEP(R, B, S, R2, B2, S2) \
+  stream_wait_barrier<2 * kC>();            \
+  issue(c + 3, R2, B2, S2);                 \
+  multiply(c, R, B, S);                     \
   ++c;
   for (int c = 0; c < nloop;) {
-    MX_STREAM_STEP(ring0, ring2)
-    MX_STREAM_STEP(ring1, ring0)
-    MX_STREAM_STEP(ring2, ring1)
+    MX_STREAM_STEP(ring0, b0, s0, ring3, b3, s3)
+    MX_STREAM_STEP(ring1, b1, s1, ring0, b0, s0)
+    MX_STREAM_STEP(ring2, b2, s2, ring1, b1, s1)
+    MX_STREAM_STEP(ring3, b3, s3, ring2, b2, s2)
   }
 #undef MX_STREAM_STEP
   // no copy may still be writing this workgroup's LDS when it ends

@@ -156,12 +156,12 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
  * many tiles.
  *
- * mode STREAM is the long-K kernel for small M: like PREQUANT it quantizes
+ * mode STREAM is the K-looping kernel for small and mid M: like PREQUANT it quantizes
  * A into the workspace first; then each workgroup of four wavefronts (one
  * group of n_tiles_per_wave 16-column tiles each) takes m_blocks 16-row
  * blocks of A over a range of k_steps_per_wave 128-K steps (a multiple of
  * 4, up to ceil(K/128) rounded up to 4), looping over it four steps at a
- * time with the operands streamed through LDS, and split_k =
+ * time (A through LDS, B straight into registers), and split_k =
  * ceil(ceil(ceil(K/128)/4) / (k_steps_per_wave/4)) workgroups cover K,
  * their fp32 partials summed by the reduce kernel (split_reduce must be
  * MXFP4_REDUCE_KERNEL).  waves_n must be 4 and waves_k 1.  Same products

@@ -123,8 +123,11 @@ def test_plan_checks(lib):
 def test_stream_plan(lib):
     """Stream-mode plan rules: four wavefronts along N, one along K, the
     workgroup's K steps a multiple of 4, split_k the workgroups that cover K
-    with them, the reduce kernel for the split; and the default plan takes the
-    mode for long K and a large B with 17 <= M <= 255 only."""
+    with them, the reduce kernel for the split; and where the default plan
+    takes the mode: M <= 255, K >= 4096; any N >= 2048 from M = 96; below
+    that only with two or four row blocks per workgroup and N >= 4096 (M >=
+    48), N >= 7168, or K >= 8192 with N x K >= 100M; at M <= 16 only against
+    a large B with long K."""
     def check(p, M, N, K):
         return lib.mxfp4_check_plan(ctypes.byref(p._c()), M, N, K)
     S = mx.MODE_STREAM
@@ -149,19 +152,40 @@ def test_stream_plan(lib):
     assert mx.prequant_workspace_bytes(M, N, K, mx.Plan(S, 4, 1, 4, 1, 32, 4, 0)) == 4 * M * N * 4
     # the default plan
     for shape in [(64, 16384, 16384), (32, 16384, 4096), (128, 8192, 8192), (96, 4096, 14336),
-                  (32, 8192, 28672), (255, 16384, 16384), (20, 12288, 12288), (17, 16384, 8192)]:
+                  (32, 8192, 28672), (255, 16384, 16384), (20, 12288, 12288), (17, 16384, 8192),
+                  (24, 16384, 4096), (96, 4096, 4096), (160, 2560, 10240), (80, 4096, 14336),
+                  (36, 5120, 20480), (16, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672)]:
         p = mx.default_plan(*shape)
         assert p.mode == S, (shape, p)
         mx.check_plan(p, *shape)
-    for shape in [(16, 16384, 16384), (32, 8192, 8192), (96, 4096, 4096), (256, 16384, 16384),
-                  (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048), (24, 16384, 4096)]:
+    for shape in [(32, 8192, 8192), (56, 5120, 5120), (40, 4096, 4096), (64, 2048, 16384),
+                  (256, 16384, 16384), (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048),
+                  (8, 16384, 8192), (14, 8192, 16384), (12, 4096, 14336), (4, 16384, 16384),
+                  (96, 1024, 16384)]:
         assert mx.default_plan(*shape).mode != S, shape
+    # the tiling: as many row blocks as M needs up to four, fewer while that
+    # needs a split with K < 20480; two tiles per wavefront from 65 rows
+    assert (mx.default_plan(64, 16384, 16384).m_blocks, mx.default_plan(64, 16384, 16384).n_tiles_per_wave) == (4, 1)
+    assert (mx.default_plan(128, 16384, 16384).m_blocks, mx.default_plan(128, 16384, 16384).n_tiles_per_wave) == (4, 2)
+    assert mx.default_plan(128, 8192, 8192).m_blocks == 4 and mx.default_plan(128, 8192, 8192).split_k == 1
+    p = mx.default_plan(80, 4096, 14336)  # four row blocks would need a split
+    assert (p.m_blocks, p.split_k) == (2, 1)
+    p = mx.default_plan(96, 2048, 16384)  # so would two
+    assert (p.m_blocks, p.split_k) == (1, 1)
+    assert mx.default_plan(64, 4096, 14336).mode != S  # one row block below M = 96
+    p = mx.default_plan(36, 5120, 20480)  # K >= 20480: keeps four row blocks and splits K
+    assert (p.m_blocks, p.split_k) == (4, 3)
 
 
 def test_small_m_rule(lib):
-    """Up to 16 rows against a large B with long K, the default plan is the
-    fused kernel with eight wavefronts along N and K split over workgroups."""
-    for M, N, K in [(1, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672), (2, 16384, 8192)]:
+    """Small M against a B with long K, where the stream mode is not taken,
+    the default plan is the fused kernel with eight wavefronts along N and K
+    split over workgroups: up to 16 rows with K >= 8192 and N x K >= 100M, or
+    K >= 14336 and N x K >= 30M; 17..32 rows with N <= 4096, K >= 8192 and
+    N x K >= 30M."""
+    for M, N, K in [(1, 16384, 16384), (4, 12288, 12288), (4, 8192, 28672), (2, 16384, 8192),
+                    (12, 16384, 8192), (8, 2048, 16384), (1, 4096, 14336), (24, 4096, 14336),
+                    (32, 4096, 8192), (20, 2048, 16384)]:
         p = mx.default_plan(M, N, K)
         assert (p.mode, p.m_blocks, p.waves_n, p.waves_k) == (mx.MODE_FUSED, 1, 8, 1), (M, N, K, p)
         assert p.k_steps_per_wave in (16, 14, 12, 8) and p.split_reduce == mx.REDUCE_KERNEL
