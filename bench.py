@@ -87,8 +87,9 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-# large shapes for --large: (M, N, K), seeded like the workloads
-LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192)]
+# large shapes for --large: (M, N, K), seeded like the workloads; the last has
+# few tiles and a long K (the tiled mode splits K over workgroups)
+LARGE = [(1024, 8192, 8192), (4096, 4096, 4096), (8192, 8192, 8192), (256, 8192, 28672)]
 # weight-streaming shapes for --stream: (M, N, K), B of 60-150 MB
 STREAM = [(1, 16384, 16384), (16, 16384, 16384), (64, 16384, 16384), (32, 28672, 8192),
           (16, 8192, 28672)]
@@ -131,8 +132,10 @@ class Case:
         self.mx.gemm(self.a, self.b_packed, self.N, out=self.c, workspace=self.ws, plan=self.plan)
 
     def launches(self):
+        # the GEMM kernel, the quantizer of A (pre-quantized, tiled, stream),
+        # the reduce kernel (split plans that use it; tiled and stream ones always)
         p = self.plan
-        return 1 + (p.mode in (2, 3)) + (p.mode in (1, 2) and p.split_k > 1 and p.split_reduce == 0)
+        return 1 + (p.mode in (2, 3, 4)) + (p.split_k > 1 and (p.mode in (3, 4) or p.split_reduce == 0))
 
 
 def time_cold(torch, flush, cases, steps, warmup):
@@ -416,7 +419,9 @@ def main(argv=None):
             steps = max(3, min(args.steps, 20))
             e, _ = time_cold(torch, flush, [c], steps, 2)
             ap = mx.quant_a_packed(c.a)
-            pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, plan=c.plan)
+            nws = mx.prequant_workspace_bytes(M, N, K, c.plan)  # split partials, allocated once
+            ws_pre = mx.new_workspace(nws, c.a.device) if nws else None
+            pre = lambda: mx.gemm_prequant(ap, M, c.b_packed, N, K, out=c.c, workspace=ws_pre, plan=c.plan)
             us_pre = time_cold_fn(torch, flush, pre, steps, 2)
             fl = 2.0 * M * N * K
             med, med_pre = statistics.median(e[w.name]), statistics.median(us_pre)
@@ -426,7 +431,7 @@ def main(argv=None):
                               "prequant_A_mfma_frac_event": round(
                                   fl / (med_pre * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}),
                   flush=True)
-            del c, ap
+            del c, ap, ws_pre
             torch.cuda.empty_cache()
 
     if args.stream:

@@ -136,12 +136,28 @@ int check_plan(const mxfp4_plan& p, int M, int N, int K, bool mode_matters,
                "plan.mode must be MXFP4_MODE_FUSED, _PREQUANT, _TILED or _STREAM (got %d)", p.mode);
   if (p.mode == MXFP4_MODE_STREAM) return check_stream_plan(p, M, N, K, bad);
   if (p.mode == MXFP4_MODE_TILED) {
-    // waves_n picks the tile width; the other fields are not used
+    // waves_n picks the tile width, split_k the workgroups along K (with
+    // split_reduce); the other fields are not used
     if (K > mx::kTiledMaxK)
       return bad(MXFP4_EINVAL, "MXFP4_MODE_TILED supports K <= %d (got %d)", mx::kTiledMaxK, K);
-    const mx::TiledGeom t = mx::tiled_geometry(M, N, K, tiled_width(p));
+    const int KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
+    if (p.split_k < 1 || p.split_k > KG)
+      return bad(MXFP4_EINVAL,
+                 "MXFP4_MODE_TILED: split_k must be in [1, %d] (whole groups of four K steps per "
+                 "workgroup; got %d)", KG, p.split_k);
+    const mx::TiledGeom t = mx::tiled_geometry(M, N, K, tiled_width(p), p.split_k);
+    if ((long long)(p.split_k - 1) * t.sps >= KS)
+      return bad(MXFP4_EINVAL,
+                 "MXFP4_MODE_TILED: split_k = %d leaves a workgroup without K steps (%d steps in "
+                 "ranges of %d)", p.split_k, KS, t.sps);
+    if (p.split_k > 1 && p.split_reduce != MXFP4_REDUCE_KERNEL)
+      return bad(MXFP4_EINVAL, "MXFP4_MODE_TILED sums split partials with the reduce kernel only");
     if (t.grid * t.threads > 0xFFFFFFFFLL)
       return bad(MXFP4_EINVAL, "grid too large (%lld workgroups of %d threads)", t.grid, t.threads);
+    if (p.split_k > 1) {
+      const long long n = (N % 4 == 0) ? (long long)M * (N / 4) : (long long)M * N;
+      if (n > 0xFFFFFFFFLL - 63) return bad(MXFP4_EINVAL, "split-K reduce grid too large (%lld threads)", n);
+    }
     return MXFP4_OK;
   }
   if (p.m_blocks < 1 || p.n_tiles_per_wave < 1 || p.waves_n < 1 || p.waves_k < 1 ||
@@ -201,6 +217,7 @@ struct WsLayout {
 WsLayout ws_layout(const mxfp4_plan& p, int M, int N, int K, bool prequant_entry) {
   WsLayout w = {0, 0, 0, false};
   if (p.mode == MXFP4_MODE_TILED) {
+    if (p.split_k > 1) w.partials = round_up((size_t)p.split_k * M * N * 4, 256);
     if (!prequant_entry) w.a = round_up(mxfp4_packed_bytes(M, K), 256);
     return w;
   }
@@ -267,14 +284,24 @@ double plan_cost(const mxfp4_plan& p, int M, int N, int K) {
 // the quantizer's launch and its A traffic at 5.7 TB/s (its measured rate),
 // then per round of up to 256 tiles 0.55 us plus, per 128-K step, 0.61 to
 // 1.03 us for a 256 x 256 tile (the slower when more CUs run at once, as the
-// clock drops) and kHalfTileStep of that for a 256 x 128 one.
+// clock drops) and kHalfTileStep of that for a 256 x 128 one.  A split of K
+// over workgroups runs split times as many workgroups of a split-th of the
+// steps (whole groups of four), then the reduce launch: 4 us plus the fp32
+// partials written and read and C at 7 TB/s (fitted to 360 timings of
+// split and unsplit tiled plans on 30 shapes with M 256..1024: picks a mean
+// 1.0 % and at most 9 % slower than the fastest tiled plan of each shape).
 constexpr double kHalfTileStep = 0.608;
-double tiled_cost(int M, int N, int K, int width) {
+double tiled_cost(int M, int N, int K, int width, int split) {
   const double tiles = ceil(M / 256.0) * ceil(N / (double)width);
-  const double rounds = ceil(tiles / 256.0);
-  double step_us = 0.613 + 0.413 * fmin(1.0, tiles / 256.0);
+  const double tasks = tiles * split;
+  const double rounds = ceil(tasks / 256.0);
+  double step_us = 0.613 + 0.413 * fmin(1.0, tasks / 256.0);
   if (width != 256) step_us *= kHalfTileStep;
-  return 10.48 + (double)M * K * 2.5 / 5.7e6 + rounds * (step_us * ceil(K / 128.0) + 0.55);
+  const double ks = ceil(K / 128.0);
+  const double sps = fmin(ks, 4.0 * ceil(ceil(ks / split) / 4.0));
+  double t = 10.48 + (double)M * K * 2.5 / 5.7e6 + rounds * (step_us * sps + 0.55);
+  if (split > 1) t += 4.0 + ((double)split * M * N * 8.0 + 2.0 * M * N) / 7.0e6;
+  return t;
 }
 
 // plan_cost is relative: it omits the launch floor and, on shapes with
@@ -321,14 +348,15 @@ mxfp4_plan model_plan(int M, int N, int K) {
   if (M >= 256 && ceil(M / 256.0) * ceil(N / 256.0) >= 16) {
     double best_abs = absolute_cost(best, M, N, K);
     mxfp4_plan pick = best;
-    for (int wn : {4, 2}) {  // 256 x 256 tiles, then 256 x 128
-      const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, wn, 1, 1, 1);
-      const double t = tiled_cost(M, N, K, tiled_width(tiled));
-      if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK && t < best_abs) {
-        best_abs = t;
-        pick = tiled;
+    for (int wn : {4, 2})  // 256 x 256 tiles, then 256 x 128
+      for (int split : {1, 2, 3, 4, 6, 8}) {
+        const mxfp4_plan tiled = make_plan(MXFP4_MODE_TILED, 1, 1, wn, 1, 1, split);
+        const double t = tiled_cost(M, N, K, tiled_width(tiled), split);
+        if (check_plan(tiled, M, N, K, true, false) == MXFP4_OK && t < best_abs) {
+          best_abs = t;
+          pick = tiled;
+        }
       }
-    }
     return pick;
   }
   return best;
@@ -403,10 +431,14 @@ mxfp4_plan stream_plan(int M, int N, int K) {
 // long K and no split of K unless K >= 20480, 0.88-1.00 (13).  Left out:
 // one row block below M = 96 (B is read once per 16 rows; 1.06-1.09 on
 // four held-out shapes), a split with K < 20480 at M <= 16 (1.20 at
-// 14x8192x16384), and smaller B at M <= 16 (up to 1.46).
+// 14x8192x16384), and smaller B at M <= 16 (up to 1.46).  M 256..512 with
+// N x K <= 70M and N <= 4096 (N <= 8192 up to M = 320): 0.51-0.98 against
+// the tiled or other pick on 25 shapes; with wider N above M = 320 it was
+// 0.95-1.03, and 1.2-1.5 at N >= 11008, which the tiled mode keeps.
 bool use_stream(int M, int N, int K) {
   const long long nk = (long long)N * K;
-  if (M > 255 || K < 4096 || nk < 16LL * 1000 * 1000) return false;
+  if (M > 512 || K < 4096 || nk < 16LL * 1000 * 1000) return false;
+  if (M > 255) return nk <= 70LL * 1000 * 1000 && N >= 2048 && (N <= 4096 || (N <= 8192 && M <= 320));
   const mxfp4_plan p = stream_plan(M, N, K);
   if (M <= 16)
     return K >= 8192 && (p.split_k == 1 || K >= 20480) &&
@@ -671,7 +703,8 @@ int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_pac
   if (p.mode == MXFP4_MODE_TILED) {
     hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_src),
                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
-                                         tiled_width(p), st);
+                                         tiled_width(p), p.split_k,
+                                         reinterpret_cast<float*>(ws + wl.part_off()), st);
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
     return ok();
   }
@@ -748,7 +781,9 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
   if (p.mode == MXFP4_MODE_TILED) {
     hipError_t e = mx::launch_gemm_tiled(static_cast<const uint8_t*>(a_packed),
                                          static_cast<const uint8_t*>(b_packed), c, ldc, M, N, K,
-                                         tiled_width(p), static_cast<hipStream_t>(stream));
+                                         tiled_width(p), p.split_k,
+                                         reinterpret_cast<float*>(ws + wl.part_off()),
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "gemm_tiled launch");
     return ok();
   }

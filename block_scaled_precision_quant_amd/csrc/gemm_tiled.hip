@@ -32,6 +32,12 @@
 // contiguous range of tiles, ordered in groups of four tile rows walked
 // column by column, so the workgroups running together on one XCD cover a
 // compact block of C and share both A rows and B columns in its L2.
+//
+// With split > 1 (shapes with too few tiles to fill the CUs) each tile's K
+// steps are shared among `split` workgroups, sps steps each (a multiple of
+// four, so every range starts a scale group), and each writes its fp32
+// tile into the partials [split][M][N] that the reduce kernel of gemm.hip
+// sums in order.
 #include "mx_internal.hpp"
 
 namespace mx {
@@ -65,9 +71,11 @@ struct TiledArgs {
   const uint8_t* ap;  // MX-packed A
   const uint8_t* bp;  // MX-packed B
   uint16_t* c;        // bf16 C [M][ldc]
+  float* ws;          // fp32 partials [split][M][N] (split > 1)
   int M, N, ldc;
   int MT, NT, KS, KG;  // A row tiles, B row tiles, K steps, scale dwords per lane
   int tiles_m, tiles_n, per_xcd;
+  int split, sps;      // workgroups per tile along K, K steps of each (a multiple of 4)
 };
 
 
@@ -111,11 +119,16 @@ void gemm_tiled_kernel(TiledArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // tile of this workgroup (see the file header)
+  // tile and K range of this workgroup (see the file header)
   const int xcd = blockIdx.x & 7;
   const int k = blockIdx.x >> 3;
-  const int tile = xcd * g.per_xcd + k;
-  if (k >= g.per_xcd || tile >= g.tiles_m * g.tiles_n) return;
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int task = xcd * g.per_xcd + k;
+  if (k >= g.per_xcd || task >= tiles * g.split) return;
+  const int s = task / tiles;
+  const int tile = task - s * tiles;
+  const int j0 = s * g.sps;                   // first K step
+  const int nsteps = min(g.sps, g.KS - j0);   // >= 1 (checked by the host)
   const int group = tile / (kGroupM * g.tiles_n);
   const int first_m = group * kGroupM;
   const int rows_in = min(kGroupM, g.tiles_m - first_m);
@@ -155,12 +168,13 @@ void gemm_tiled_kernel(TiledArgs g) {
     sb_[r] = tb * g.KS * kBlockBytes;
     ssb_[r] = tb * g.KG * 256;
   }
-  const int last = g.KS - 1;
-  // copy step jj (clamped to the last) into stage ST: 4 instructions, 8
-  // when SC (jj % 4 == 0) adds the scale dwords of its group of four steps
+  const int last = nsteps - 1;
+  // copy step j0 + jj (jj clamped to the last) into stage ST: 4
+  // instructions, 8 when SC (jj % 4 == 0) adds the scale dwords of its
+  // group of four steps
 #define MX_DMA(ST, jj, SC)                                                                       \
   {                                                                                              \
-    const int js = min((jj), last);                                                              \
+    const int js = j0 + min((jj), last);                                                         \
     const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
     _Pragma("unroll") for (int r = 0; r < kRA; ++r) {                                            \
       dma16(ra, ST + kStageA + (wave + kWaves * r) * 1024, lane16, sa_[r] + od);                 \
@@ -279,15 +293,15 @@ void gemm_tiled_kernel(TiledArgs g) {
   MX_READ(p, g_stage0, 0, true)
   MX_READ(q, g_stage0, 1, true)
   int j = 0;
-  for (; j + 3 < g.KS; j += 4) {
+  for (; j + 3 < nsteps; j += 4) {
     MX_STEP(0, j, g_stage0, g_stage1, 2 * kC)
     MX_STEP(1, j + 1, g_stage1, g_stage2, 3 * kC)
     MX_STEP(2, j + 2, g_stage2, g_stage3, 3 * kC)
     MX_STEP(3, j + 3, g_stage3, g_stage0, 2 * kC)
   }
-  if (j < g.KS) MX_STEP(0, j, g_stage0, g_stage1, 2 * kC)
-  if (j + 1 < g.KS) MX_STEP(1, j + 1, g_stage1, g_stage2, 3 * kC)
-  if (j + 2 < g.KS) MX_STEP(2, j + 2, g_stage2, g_stage3, 3 * kC)
+  if (j < nsteps) MX_STEP(0, j, g_stage0, g_stage1, 2 * kC)
+  if (j + 1 < nsteps) MX_STEP(1, j + 1, g_stage1, g_stage2, 3 * kC)
+  if (j + 2 < nsteps) MX_STEP(2, j + 2, g_stage2, g_stage3, 3 * kC)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the loop
 #undef MX_STEP
 #undef MX_BARRIER
@@ -307,6 +321,36 @@ void gemm_tiled_kernel(TiledArgs g) {
   // stores); otherwise each value goes out on its own.
   const int row0 = tm * kTileM + 32 * kU * wm;
   const int col0 = tn * kTN + 64 * wn;
+  if (g.split > 1) {
+    // fp32 partial of this K range: lane L holds row L%32 of each 32-row
+    // block and four neighbouring columns per register group, one 16-byte
+    // store each where N allows
+    float* part = g.ws + (size_t)s * g.M * g.N;
+    const int lrow0 = row0 + (lane & 31);
+    const int lcol0 = col0 + 4 * (lane >> 5);
+    const bool vec4 = (g.N % 4) == 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int row = lrow0 + 32 * u;
+      if (row >= g.M) continue;
+      float* prow = part + (size_t)row * g.N;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = lcol0 + 32 * v + 8 * q;
+          if (vec4 && col + 3 < g.N) {
+            *reinterpret_cast<f32x4*>(prow + col) =
+                f32x4{acc[u][v][4 * q], acc[u][v][4 * q + 1], acc[u][v][4 * q + 2], acc[u][v][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < g.N) prow[col + e] = acc[u][v][4 * q + e];
+          }
+        }
+    }
+    return;
+  }
   const bool vec = (g.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
                    (tn + 1) * kTN <= g.N;
   if (vec) {
@@ -358,27 +402,32 @@ void gemm_tiled_kernel(TiledArgs g) {
   }
 }
 
-TiledGeom tiled_geometry(int M, int N, int K, int tile_n) {
+TiledGeom tiled_geometry(int M, int N, int K, int tile_n, int split) {
   TiledGeom t;
   t.tiles_m = (int)(((long long)M + kTileM - 1) / kTileM);
   t.tiles_n = (int)(((long long)N + tile_n - 1) / tile_n);
-  const long long tiles = (long long)t.tiles_m * t.tiles_n;
-  t.per_xcd = (int)((tiles + 7) / 8);
+  const long long tasks = (long long)t.tiles_m * t.tiles_n * split;
+  t.per_xcd = (int)((tasks + 7) / 8);
   t.grid = 8LL * t.per_xcd;
   t.threads = 512;  // eight wavefronts for either width
   t.lds = 0;  // static: the four stages
-  (void)K;
+  const long long KS = ((long long)K + 127) / 128;
+  t.sps = (int)(4 * (((KS + split - 1) / split + 3) / 4));
   return t;
 }
 
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
-                             int M, int N, int K, int tile_n, hipStream_t stream) {
-  const TiledGeom t = tiled_geometry(M, N, K, tile_n);
+                             int M, int N, int K, int tile_n, int split, float* ws,
+                             hipStream_t stream) {
+  const TiledGeom t = tiled_geometry(M, N, K, tile_n, split);
   const PackedDims da = packed_dims(M, K), db = packed_dims(N, K);
   TiledArgs args;
   args.ap = a_packed;
   args.bp = b_packed;
   args.c = c;
+  args.ws = ws;
+  args.split = split;
+  args.sps = t.sps;
   args.M = M;
   args.N = N;
   args.ldc = ldc;
@@ -392,8 +441,10 @@ hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, u
   void* kargs[] = {&args};
   const void* fn = tile_n == 128 ? reinterpret_cast<const void*>(&gemm_tiled_kernel<128, 2>)
                                   : reinterpret_cast<const void*>(&gemm_tiled_kernel<256, 4>);
-  return hipLaunchKernel(fn, dim3((unsigned)t.grid),
-                         dim3(t.threads), kargs, (unsigned)t.lds, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3(t.threads), kargs, (unsigned)t.lds, stream);
+  if (err != hipSuccess) return err;
+  if (split > 1) return launch_splitk_reduce(ws, c, M, N, ldc, split, stream);
+  return hipSuccess;
 }
 
 }  // namespace mx

@@ -68,15 +68,20 @@ hipError_t launch_gemm(const Plan& p, const void* a, int lda, const uint8_t* b_p
 // Longest K of the tiled kernel: its buffer offsets within one workgroup's
 // 16 row tiles stay below 2^31.
 constexpr int kTiledMaxK = 1 << 22;
+// split > 1 shares each tile's K among split workgroups of sps steps (a
+// multiple of 4), whose fp32 partials [split][M][N] in ws the reduce kernel
+// sums.
 struct TiledGeom {
   int tiles_m, tiles_n, per_xcd;
   long long grid;  // workgroups
   int threads;
   int lds;         // bytes of LDS per workgroup
+  int sps;         // K steps per workgroup
 };
-TiledGeom tiled_geometry(int M, int N, int K, int tile_n);
+TiledGeom tiled_geometry(int M, int N, int K, int tile_n, int split);
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
-                             int M, int N, int K, int tile_n, hipStream_t stream);
+                             int M, int N, int K, int tile_n, int split, float* ws,
+                             hipStream_t stream);
 
 // Sum fp32 partials [S][M][N] in order s = 0..S-1 into bf16 C (gemm.hip).
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* c, int M, int N, int ldc, int S,

@@ -150,11 +150,16 @@ int mxfp4_quant_a_packed(const uint16_t *a, int M, int K, int lda, void *out_pac
  * workspace first, then one workgroup computes each tile of C over the
  * whole of K with the gfx950 block-scaled 32x32x64 FP4 instruction (the
  * same products and fp32 sums per output as the other modes, in K order;
- * results agree with them within fp32 rounding, not bit for bit).  Only
- * waves_n is read: waves_n == 2 selects 256 x 128 tiles, any other value
- * 256 x 256 tiles (eight wavefronts either way); both widths give the same
- * bits.  K must be <= 4194304 (2^22).  It pays off when M and N give
- * many tiles.
+ * results agree with them within fp32 rounding, not bit for bit).
+ * waves_n == 2 selects 256 x 128 tiles, any other value 256 x 256 tiles
+ * (eight wavefronts either way); both widths give the same bits.  split_k
+ * > 1 shares each tile's K among split_k workgroups of
+ * 4*ceil(ceil(ceil(K/128)/split_k)/4) steps each (none may be left empty:
+ * split_k <= ceil(ceil(K/128)/4) and (split_k-1) times that < ceil(K/128)),
+ * whose fp32 partials [split_k][M][N] in the workspace the reduce kernel
+ * sums in order (split_reduce must be MXFP4_REDUCE_KERNEL).  The other
+ * fields are not read.  K must be <= 4194304 (2^22).  It pays off when M
+ * and N give many tiles, or, split, when K is long.
  *
  * mode STREAM is the K-looping kernel for small and mid M: like PREQUANT it quantizes
  * A into the workspace first; then each workgroup of four wavefronts (one

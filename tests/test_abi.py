@@ -154,14 +154,16 @@ def test_stream_plan(lib):
     for shape in [(64, 16384, 16384), (32, 16384, 4096), (128, 8192, 8192), (96, 4096, 14336),
                   (32, 8192, 28672), (255, 16384, 16384), (20, 12288, 12288), (17, 16384, 8192),
                   (24, 16384, 4096), (96, 4096, 4096), (160, 2560, 10240), (80, 4096, 14336),
-                  (36, 5120, 20480), (16, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672)]:
+                  (36, 5120, 20480), (16, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672),
+                  (256, 4096, 11008), (512, 3072, 12288), (320, 7168, 7168), (256, 8192, 8192)]:
         p = mx.default_plan(*shape)
         assert p.mode == S, (shape, p)
         mx.check_plan(p, *shape)
     for shape in [(32, 8192, 8192), (56, 5120, 5120), (40, 4096, 4096), (64, 2048, 16384),
                   (256, 16384, 16384), (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048),
                   (8, 16384, 8192), (14, 8192, 16384), (12, 4096, 14336), (4, 16384, 16384),
-                  (96, 1024, 16384)]:
+                  (96, 1024, 16384), (384, 12288, 4096), (448, 7168, 7168), (256, 16384, 16384),
+                  (513, 4096, 8192)]:
         assert mx.default_plan(*shape).mode != S, shape
     # the tiling: as many row blocks as M needs up to four, fewer while that
     # needs a split with K < 20480; two tiles per wavefront from 65 rows
@@ -194,16 +196,37 @@ def test_small_m_rule(lib):
 
 
 def test_tiled_plan(lib):
-    # the tiled mode has a fixed tiling: the other fields are not checked
-    M, N, K = 300, 520, 640
-    for fields in [(1, 1, 1, 1, 1, 1), (0, 0, 0, 0, 0, 0), (3, 7, 99, -1, 5, 2)]:
-        p = mx.Plan(mx.MODE_TILED, *fields, 9)
+    # the tiled mode has a fixed tiling: waves_n picks the width and split_k
+    # (with split_reduce) the workgroups along K; the other fields are not
+    # checked
+    M, N, K = 300, 520, 640  # 5 K steps
+    for fields in [(1, 1, 1, 1, 1), (0, 0, 0, 0, 0), (3, 7, 99, -1, 5)]:
+        p = mx.Plan(mx.MODE_TILED, *fields, 1, 9)
         assert lib.mxfp4_check_plan(ctypes.byref(p._c()), M, N, K) == 0
         # workspace: the MX-packed A only, nothing to zero-fill; none when A
         # comes pre-quantized
         assert mx.workspace_bytes(M, N, K, p) == (mx.packed_bytes(M, K) + 255) // 256 * 256
         assert mx.workspace_zero_bytes(M, N, K, p) == 0
         assert mx.prequant_workspace_bytes(M, N, K, p) == 0
+    # split of K: whole groups of four steps per workgroup, none empty, the
+    # reduce kernel; the workspace adds the fp32 partials
+    def check(split, reduce=0, shape=(M, N, K)):
+        p = mx.Plan(mx.MODE_TILED, 1, 1, 4, 1, 1, split, reduce)
+        return lib.mxfp4_check_plan(ctypes.byref(p._c()), *shape)
+    assert check(2) == 0                      # steps 0-3 and 4
+    assert check(3) == EINVAL                 # 5 steps hold two groups of four
+    assert check(0) == EINVAL
+    assert check(2, mx.REDUCE_LAST_WG) == EINVAL
+    assert check(2, mx.REDUCE_ATOMIC) == EINVAL
+    assert check(4, 0, (300, 520, 3072)) == EINVAL   # 24 steps in ranges of 8: the 4th is empty
+    assert "without K steps" in mx.load().mxfp4_last_error().decode()
+    assert check(3, 0, (300, 520, 3072)) == 0
+    assert check(8, 0, (300, 520, 4096)) == 0        # 32 steps: ranges of 4
+    p = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 2, 0)
+    a = (mx.packed_bytes(M, K) + 255) // 256 * 256
+    assert mx.workspace_bytes(M, N, K, p) == 2 * M * N * 4 + a
+    assert mx.prequant_workspace_bytes(M, N, K, p) == 2 * M * N * 4
+    assert mx.workspace_zero_bytes(M, N, K, p) == 0
     # 2^20 x 2^19 is 2^23 tiles of 512 threads: one work-item more than a
     # dispatch holds; one tile column fewer fits.  The 256 x 128 tiles
     # (waves_n == 2) also have 512 threads: half the columns fit.
@@ -346,6 +369,12 @@ def test_default_plan_mode_by_size(lib):
         p = mx.default_plan(M, N, K)
         assert p.mode == mx.MODE_TILED and (p.waves_n != 2) == wide, (M, N, K, p)
         assert mx.workspace_bytes(M, N, K) == mx.packed_bytes(M, K) + (-mx.packed_bytes(M, K) % 256)
+    # few tiles and a long K: K split over workgroups (measured 0.53-0.94 of
+    # the whole-K tiled plan's time on 18 such shapes)
+    for M, N, K in [(256, 8192, 28672), (256, 5120, 20480), (640, 2048, 8192), (1024, 3072, 12288)]:
+        p = mx.default_plan(M, N, K)
+        assert p.mode == mx.MODE_TILED and p.split_k > 1 and p.split_reduce == mx.REDUCE_KERNEL, (M, N, K, p)
+        assert mx.workspace_bytes(M, N, K) > mx.packed_bytes(M, K) + p.split_k * M * N * 4 - 1
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch(lib):

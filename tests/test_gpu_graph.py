@@ -37,6 +37,7 @@ CASES = [
     ((256, 3072, 1536), mx.Plan(P, 2, 1, 6, 1, 12, 1)),                # quantizer + GEMM
     ((520, 512, 800), mx.Plan(T, 1, 1, 1, 1, 1, 1)),                   # tiled 256 x 256
     ((520, 512, 800), mx.Plan(T, 1, 1, 2, 1, 1, 1)),                   # tiled 256 x 128
+    ((520, 512, 1024), mx.Plan(T, 1, 1, 2, 1, 1, 2, mx.REDUCE_KERNEL)),  # tiled, K split in two
     ((32, 8192, 28672), None),                                         # default: stream, split 2 + reduce
     ((40, 520, 4096), mx.Plan(mx.MODE_STREAM, 4, 1, 4, 1, 16, 2, 0)),  # stream, ragged M and N
     ((16, 2112, 7168), NOALLOC),                                       # split-K partials in the array

@@ -6,7 +6,9 @@ elementwise.  Shapes cover one 256 x 256 tile, ragged M and N edges inside a
 tile, K that ends inside a 128-element step, step counts that leave 0 to 3
 steps after the kernel's last group of four, grids whose tile count is not
 a multiple of the 8 XCD slots (some workgroups have no tile), and sampled
-outputs of large shapes.
+outputs of large shapes; with K split over workgroups (fp32 partials and
+the reduce kernel), ranges that end inside a group of four steps or hold a
+single step, N not a multiple of 4, and the prequant entry.
 """
 import numpy as np
 import pytest
@@ -151,4 +153,67 @@ def test_tiled_large_sampled(M, N, K, plan):
     r = torch.as_tensor(rows, device=c.device)
     q = torch.as_tensor(cols, device=c.device)
     assert_close_to_oracle(bf16_out_to_f32(c[r][:, q]), want, "tiled %dx%dx%d sampled" % (M, N, K))
+    assert not torch.isnan(c).any().item()
+
+
+@pytest.mark.parametrize("M,N,K,split", [
+    (300, 520, 640, 2),     # 5 K steps: ranges of 4 and 1
+    (257, 272, 1504, 3),    # K ends inside the 12th step: three ranges of 4
+    (513, 1000, 2080, 3),   # 17 steps: 8, 8 and 1; N not a multiple of 16
+    (300, 518, 640, 2),     # N % 4 != 0: partials stored value by value
+    (768, 768, 4096, 8),    # 32 steps: eight ranges of 4; 9 tiles x 8 workgroups
+    (256, 256, 128, 1),
+])
+@WIDTHS
+def test_tiled_split_oracle(M, N, K, split, plan):
+    """K shared among split workgroups per tile, fp32 partials summed by the
+    reduce kernel: within the GEMM tolerance of the oracle."""
+    p = mx.Plan(mx.MODE_TILED, 1, 1, plan.waves_n, 1, 1, split, mx.REDUCE_KERNEL)
+    print("case tiled split", M, N, K, split, plan.waves_n, flush=True)
+    ref = reference((M, N, K, M * 5 + split))
+    assert_close_to_oracle(run_gemm(ref, p), ref["c32"], "tiled split %dx%dx%d %s" % (M, N, K, p))
+
+
+def test_tiled_split_prequant_and_no_stale_partials():
+    """The prequant entry with a split tiled plan equals the fused-entry call
+    bit for bit; on one workspace, A then -A gives exactly -C (every partial
+    is rewritten by each call)."""
+    M, N, K = 520, 300, 3072  # 24 steps: three ranges of 8
+    p = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 3, mx.REDUCE_KERNEL)
+    ref = reference((M, N, K, 17))
+    a = to_dev_bf16(ref["a_bits"])
+    b_packed = mx.pack_b(to_dev_u8(ref["bq"]), to_dev_u8(ref["bs"]))
+    ws = mx.new_workspace(mx.workspace_bytes(M, N, K, p), a.device)
+    c1 = mx.gemm(a, b_packed, N, workspace=ws, plan=p)
+    c2 = mx.gemm(-a, b_packed, N, workspace=ws, plan=p)
+    ap = mx.quant_a_packed(a)
+    c3 = mx.gemm_prequant(ap, M, b_packed, N, K, plan=p)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bf16_out_to_f32(c1), ref["c32"], "tiled split")
+    # values, not bits: an output whose products cancel exactly is +0 for A and for -A
+    assert np.array_equal(bf16_out_to_f32(c2), -bf16_out_to_f32(c1))
+    assert torch.equal(c1.view(torch.int16), c3.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,split", [(256, 8192, 28672, 4), (384, 4104, 16384, 3)])
+def test_tiled_split_large_sampled(M, N, K, split):
+    p = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, split, mx.REDUCE_KERNEL)
+    print("case tiled split sampled", M, N, K, split, flush=True)
+    a, b = inputs.make_shape(M, N, K, seed=(M * 7 + N) % 1000)
+    aq, asc = oracle.quantize(a)
+    bq, bsc = oracle.quantize(b)
+    dev_a = to_dev_bf16(a)
+    b_packed = mx.pack_b(to_dev_u8(bq), to_dev_u8(bsc))
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev_a.device)
+    mx.gemm(dev_a, b_packed, N, out=c, plan=p)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1, M // 2], rng.integers(0, M, 11)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, N - 1, N // 2], rng.integers(0, N, 61)]))
+    rows, cols = rows[rows < M], cols[cols < N]
+    want, _ = oracle.gemm(oracle.dequantize(aq[rows], asc[rows]), oracle.dequantize(bq[cols], bsc[cols]),
+                          want64=False)
+    r = torch.as_tensor(rows, device=c.device)
+    q = torch.as_tensor(cols, device=c.device)
+    assert_close_to_oracle(bf16_out_to_f32(c[r][:, q]), want, "tiled split %dx%dx%d sampled" % (M, N, K))
     assert not torch.isnan(c).any().item()
