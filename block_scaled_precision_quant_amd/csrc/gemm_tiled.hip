@@ -407,8 +407,9 @@ TiledGeom tiled_geometry(int M, int N, int K, int tile_n, int split) {
   t.tiles_m = (int)(((long long)M + kTileM - 1) / kTileM);
   t.tiles_n = (int)(((long long)N + tile_n - 1) / tile_n);
   const long long tasks = (long long)t.tiles_m * t.tiles_n * split;
-  t.per_xcd = (int)((tasks + 7) / 8);
-  t.grid = 8LL * t.per_xcd;
+  const long long per_xcd = (tasks + 7) / 8;
+  t.grid = 8LL * per_xcd;  // the host refuses grids past 2^32 work-items before per_xcd is used
+  t.per_xcd = (int)(per_xcd < 0x7FFFFFFF ? per_xcd : 0x7FFFFFFF);
   t.threads = 512;  // eight wavefronts for either width
   t.lds = 0;  // static: the four stages
   const long long KS = ((long long)K + 127) / 128;

@@ -222,6 +222,10 @@ def test_tiled_plan(lib):
     assert "without K steps" in mx.load().mxfp4_last_error().decode()
     assert check(3, 0, (300, 520, 3072)) == 0
     assert check(8, 0, (300, 520, 4096)) == 0        # 32 steps: ranges of 4
+    # 2^20 tiles of 256 x 256 times a split of 8192 (K = 2^22) is 2^33
+    # workgroups, past 2^32 work-items: refused
+    assert check(8192, 0, (1 << 18, 1 << 18, 1 << 22)) == EINVAL
+    assert "grid too large" in mx.load().mxfp4_last_error().decode()
     p = mx.Plan(mx.MODE_TILED, 1, 1, 2, 1, 1, 2, 0)
     a = (mx.packed_bytes(M, K) + 255) // 256 * 256
     assert mx.workspace_bytes(M, N, K, p) == 2 * M * N * 4 + a
