@@ -64,16 +64,19 @@ __shared__ __align__(16) uint8_t g_stage1[kStageBytes];
 __shared__ __align__(16) uint8_t g_stage2[kStageBytes];
 __shared__ __align__(16) uint8_t g_stage3[kStageBytes];
 
-// B's copies with the nontemporal hint, for grids of at most four row tiles,
-// where each B byte is read by so few workgroups that it streams from HBM:
+// Copies with the nontemporal hint, for an operand that so few workgroups
+// read that it streams from HBM.  B's, for grids of at most four row tiles:
 // 8-18 % less time per call at 1024x8192x8192, 768x8192x8192,
 // 256x4096x14336 and the split 256/512 x 8192 x 28672 plans, 2-4 % at
 // 1024x16384x16384 and 384x16384x16384; with 16 and 32 row tiles (4096^3,
 // 8192^3), whose B columns many tiles re-read from the L2, it cost 2-3 %.
+// A's, for grids of at most eight column tiles: 4-7 % at 8192x1024x8192,
+// 16384x512x4096 and 4096x1024x16384; with 64 it cost 13 %.
 __device__ inline void dma16_nt(BufRsrc r, uint8_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, voff, soff, 0, kCachePolicyNT);
 }
 constexpr int kNtMaxRowTiles = 4;
+constexpr int kNtMaxColTiles = 8;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -118,7 +121,7 @@ __device__ inline void wait_copies_barrier() {
     asm volatile("s_waitcnt vmcnt(18)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int kTN, int kU, bool kNtB>
+template <int kTN, int kU, bool kNtA, bool kNtB>
 __global__ __launch_bounds__(kTN * 8 / kU) __attribute__((amdgpu_waves_per_eu(kTN / (32 * kU), kTN / (32 * kU))))
 void gemm_tiled_kernel(TiledArgs g) {
   constexpr int kWavesN = kTN / 64;       // wavefronts along N (64 columns each)
@@ -188,7 +191,8 @@ void gemm_tiled_kernel(TiledArgs g) {
     const int js = j0 + min((jj), last);                                                         \
     const int od = js * kBlockBytes, os = (js >> 2) * 256;                                       \
     _Pragma("unroll") for (int r = 0; r < kRA; ++r) {                                            \
-      dma16(ra, ST + kStageA + (wave + kWaves * r) * 1024, lane16, sa_[r] + od);                 \
+      if constexpr (kNtA) dma16_nt(ra, ST + kStageA + (wave + kWaves * r) * 1024, lane16, sa_[r] + od); \
+      else dma16(ra, ST + kStageA + (wave + kWaves * r) * 1024, lane16, sa_[r] + od);            \
       if (SC) dma4(ras, ST + kStageAS + (wave + kWaves * r) * 256, lane4, ssa_[r] + os);         \
     }                                                                                            \
     _Pragma("unroll") for (int r = 0; r < kRB; ++r) {                                            \
@@ -429,6 +433,14 @@ TiledGeom tiled_geometry(int M, int N, int K, int tile_n, int split) {
   return t;
 }
 
+template <int kTN, int kU>
+static const void* tiled_kernel_fn(bool nt_a, bool nt_b) {
+  if (nt_a) return nt_b ? reinterpret_cast<const void*>(&gemm_tiled_kernel<kTN, kU, true, true>)
+                        : reinterpret_cast<const void*>(&gemm_tiled_kernel<kTN, kU, true, false>);
+  return nt_b ? reinterpret_cast<const void*>(&gemm_tiled_kernel<kTN, kU, false, true>)
+              : reinterpret_cast<const void*>(&gemm_tiled_kernel<kTN, kU, false, false>);
+}
+
 hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, uint16_t* c, int ldc,
                              int M, int N, int K, int tile_n, int split, float* ws,
                              hipStream_t stream) {
@@ -452,11 +464,8 @@ hipError_t launch_gemm_tiled(const uint8_t* a_packed, const uint8_t* b_packed, u
   args.tiles_n = t.tiles_n;
   args.per_xcd = t.per_xcd;
   void* kargs[] = {&args};
-  const bool nt_b = t.tiles_m <= kNtMaxRowTiles;
-  const void* fn = tile_n == 128 ? (nt_b ? reinterpret_cast<const void*>(&gemm_tiled_kernel<128, 2, true>)
-                                         : reinterpret_cast<const void*>(&gemm_tiled_kernel<128, 2, false>))
-                                 : (nt_b ? reinterpret_cast<const void*>(&gemm_tiled_kernel<256, 4, true>)
-                                         : reinterpret_cast<const void*>(&gemm_tiled_kernel<256, 4, false>));
+  const bool nt_a = t.tiles_n <= kNtMaxColTiles, nt_b = t.tiles_m <= kNtMaxRowTiles;
+  const void* fn = tile_n == 128 ? tiled_kernel_fn<128, 2>(nt_a, nt_b) : tiled_kernel_fn<256, 4>(nt_a, nt_b);
   hipError_t err = hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3(t.threads), kargs, (unsigned)t.lds, stream);
   if (err != hipSuccess) return err;
   if (split > 1) return launch_splitk_reduce(ws, c, M, N, ldc, split, stream);
