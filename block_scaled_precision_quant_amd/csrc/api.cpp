@@ -432,13 +432,20 @@ mxfp4_plan stream_plan(int M, int N, int K) {
 // one row block below M = 96 (B is read once per 16 rows; 1.06-1.09 on
 // four held-out shapes), a split with K < 20480 at M <= 16 (1.20 at
 // 14x8192x16384), and smaller B at M <= 16 (up to 1.46).  M 256..512 with
-// N x K <= 70M and N <= 4096 (N <= 8192 up to M = 320): 0.51-0.98 against
-// the tiled or other pick on 25 shapes; with wider N above M = 320 it was
-// 0.95-1.03, and 1.2-1.5 at N >= 11008, which the tiled mode keeps.
+// N x K <= 70M and N <= 8192 (M = 256), N <= 6144 (up to M = 320), or N <=
+// 4096 and N x K <= 40M: 0.51-0.98 against the tiled or other pick on 25
+// shapes, 0.74-0.89 against the fastest tiled plan (nontemporal copies, any
+// split) on seven; beyond those bounds the tiled mode won (by 5 % at
+// 384/512 x 4096 x 11008, 12 % at 320 x 7168 x 7168, 20-50 % at N >= 11008).
 bool use_stream(int M, int N, int K) {
   const long long nk = (long long)N * K;
   if (M > 512 || K < 4096 || nk < 16LL * 1000 * 1000) return false;
-  if (M > 255) return nk <= 70LL * 1000 * 1000 && N >= 2048 && (N <= 4096 || (N <= 8192 && M <= 320));
+  if (M > 255) {
+    if (nk > 70LL * 1000 * 1000 || N < 2048) return false;
+    if (M <= 256) return N <= 8192;
+    if (M <= 320) return N <= 6144;
+    return N <= 4096 && nk <= 40LL * 1000 * 1000;
+  }
   const mxfp4_plan p = stream_plan(M, N, K);
   if (M <= 16)
     return K >= 8192 && (p.split_k == 1 || K >= 20480) &&

@@ -155,7 +155,7 @@ def test_stream_plan(lib):
                   (32, 8192, 28672), (255, 16384, 16384), (20, 12288, 12288), (17, 16384, 8192),
                   (24, 16384, 4096), (96, 4096, 4096), (160, 2560, 10240), (80, 4096, 14336),
                   (36, 5120, 20480), (16, 16384, 16384), (8, 12288, 12288), (16, 8192, 28672),
-                  (256, 4096, 11008), (512, 3072, 12288), (320, 7168, 7168), (256, 8192, 8192)]:
+                  (256, 4096, 11008), (512, 3072, 12288), (320, 6144, 6144), (256, 8192, 8192)]:
         p = mx.default_plan(*shape)
         assert p.mode == S, (shape, p)
         mx.check_plan(p, *shape)
@@ -163,7 +163,7 @@ def test_stream_plan(lib):
                   (256, 16384, 16384), (64, 16384, 2048), (16, 2112, 7168), (64, 7168, 2048),
                   (8, 16384, 8192), (14, 8192, 16384), (12, 4096, 14336), (4, 16384, 16384),
                   (96, 1024, 16384), (384, 12288, 4096), (448, 7168, 7168), (256, 16384, 16384),
-                  (513, 4096, 8192)]:
+                  (513, 4096, 8192), (320, 7168, 7168), (384, 4096, 11008)]:
         assert mx.default_plan(*shape).mode != S, shape
     # the tiling: as many row blocks as M needs up to four, fewer while that
     # needs a split with K < 20480; two tiles per wavefront from 65 rows
