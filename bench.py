@@ -190,12 +190,16 @@ def trimmed_mean(us):
 
 
 def kernel_sources_sha():
-    """sha256 over the HIP sources; hardware counters recorded under
-    profiles/ are only reported while the kernels are unchanged."""
+    """sha256 over the device sources (the .hip files and the headers they
+    share); hardware counters recorded under profiles/ are only reported
+    while the kernels are unchanged.  The host-side plan choice (api.cpp) is
+    checked per shape instead: see recorded_profiles."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_precision_quant_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".hpp")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -206,7 +210,9 @@ def recorded_profiles():
     per shape the traced kernel durations, HBM bytes per call from the
     FETCH_SIZE/WRITE_SIZE runs and, for the compute-leaning shape, matrix-core
     counters; the empty-kernel durations of the same trace), only while the
-    kernel sources hash to the sha it was taken with; {} otherwise."""
+    kernel sources hash to the sha it was taken with ({} otherwise), and of
+    those shapes only the ones whose default plan is still the plan recorded
+    with them."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -215,7 +221,13 @@ def recorded_profiles():
         return {}
     if rec.get("kernel_sources_sha") != kernel_sources_sha():
         return {}
-    return rec
+    import block_scaled_precision_quant_amd as mx
+    keep = {}
+    for name, e in rec.get("shapes", {}).items():
+        w = inputs.WORKLOADS.get(name)
+        if w is not None and e.get("plan") == mx.default_plan(w.M, w.N, w.K).__dict__:
+            keep[name] = e
+    return dict(rec, shapes=keep)
 
 
 def shape_label(c):

@@ -405,8 +405,8 @@ int stream_split(int M, int N, int K, int mbw, int ntw) {
 // smallest split that gives 192 workgroups.  On the 225 training shapes of
 // the rule below this pick was a mean 0.3 % (at most 6 %) slower than the
 // fastest of the six tilings with one, two or four row blocks and one or two
-// tiles per wavefront; on ten held-out shapes where only the tiles per
-// wavefront differ from the previous rule's pick, 0.90-1.06 of its time.
+// tiles per wavefront; on ten held-out shapes with M >= 112 where it takes
+// two tiles per wavefront, 0.90-1.06 of the time with one.
 mxfp4_plan stream_plan(int M, int N, int K) {
   const int MT = (M + 15) / 16, KS = (int)(((long long)K + 127) / 128), KG = (KS + 3) / 4;
   int mbw = MT <= 2 ? MT : 4;

@@ -51,8 +51,10 @@ def test_alternative_plans_are_valid():
 def test_recorded_profile_matches_the_kernel_sources():
     """profiles/traffic.json (the rocprofv3 record bench.py reads for kernel
     durations, HBM bytes and counters) was taken with the current kernel
-    sources and covers every benchmark shape; a kernel change without a new
-    profile fails here, before a bench line reports stale figures."""
+    sources and covers every benchmark shape with the plan its default still
+    is; a kernel change, or a plan-rule change that moves a benchmark shape,
+    without a new profile fails here, before a bench line reports stale
+    figures."""
     from block_scaled_precision_quant_amd import inputs
     rec = bench.recorded_profiles()
     assert rec, "profiles/traffic.json is missing or was taken with other kernel sources"
