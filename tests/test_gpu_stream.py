@@ -5,7 +5,9 @@ The library quantizes B on the GPU and packs it (as a caller would); the
 oracle quantizes, from the same bf16 inputs, only the sampled rows of B and
 the rows of A, and takes their fp32 dot products.  The plans are the default
 one and the split-K plans these sizes run (long K split over workgroups, the
-fp32 partials summed by the reduce kernel).  Same bar as every GEMM parity
+fp32 partials summed by the reduce kernel); default-plan cases assert the
+mode they exercise (the stream kernel with one row block, at M 256..512,
+and the tiled kernel with a split of K).  Same bar as every GEMM parity
 test: |C_gpu - C_ref| <= 1e-2*|C_ref| + 1e-2 elementwise; C is poisoned with
 NaN first and must hold no NaN afterwards.
 """
@@ -28,7 +30,14 @@ CASES = [
     ((1, 16384, 16384), mx.Plan(F, 1, 1, 7, 1, 16, 8, 0)),    # fused, 8-way split
     ((16, 8192, 28672), None),                                # default plan, 224 K steps
     ((32, 28672, 8192), mx.Plan(P, 2, 1, 4, 2, 16, 2, 0)),    # pre-quantized A, 2-way split
+    ((16, 16384, 16384), None),                               # default: stream, one row block
+    ((300, 2048, 8192), None),                                # default: stream at M 256..512, ragged M
+    ((256, 8192, 28672), None),                               # default: tiled, K split, B nontemporal
 ]
+# the mode each default-plan case is meant to exercise
+EXPECT = {(64, 16384, 16384): mx.MODE_STREAM, (16, 8192, 28672): mx.MODE_STREAM,
+          (16, 16384, 16384): mx.MODE_STREAM, (300, 2048, 8192): mx.MODE_STREAM,
+          (256, 8192, 28672): mx.MODE_TILED}
 
 
 def _id(case):
@@ -41,6 +50,8 @@ def _id(case):
 def test_stream_shape_sampled(case):
     (M, N, K), plan = case
     print("case stream", M, N, K, plan or mx.default_plan(M, N, K), flush=True)
+    if plan is None:
+        assert mx.default_plan(M, N, K).mode == EXPECT[(M, N, K)]
     a, b = inputs.make_shape(M, N, K, seed=(M + N + K) % 997)
     dev_a = to_dev_bf16(a)
     dev_b = to_dev_bf16(b)
