@@ -393,6 +393,14 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
     rc = lib.mxfp4_gemm_noalloc(a, K, bp, mx.packed_bytes(N, K), c, N, M, N, K, None)
     assert rc == EWORKSPACE
     assert b"mxfp4_gemm with a workspace" in lib.mxfp4_last_error()
+    # a tiled plan that splits K keeps fp32 partials of every split: at
+    # 256x8192x28672 (split 4) 32 MiB of them, beyond the array as well
+    M, N, K = 256, 8192, 28672
+    p = mx.default_plan(M, N, K)
+    assert p.mode == mx.MODE_TILED and p.split_k > 1
+    assert lib.mxfp4_gemm_workspace_bytes(M, N, K) > cap
+    assert lib.mxfp4_gemm_noalloc(a, K, bp, mx.packed_bytes(N, K), c, N, M, N, K, None) == EWORKSPACE
+    M, N, K = 4096, 8192, 8192
     # argument errors come first, as for mxfp4_gemm
     assert lib.mxfp4_gemm_noalloc(None, K, bp, mx.packed_bytes(N, K), c, N, M, N, K, None) == ENULL
     assert lib.mxfp4_gemm_noalloc(a, K, bp, 16, c, N, 16, N, K, None) == ESIZE

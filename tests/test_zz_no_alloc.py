@@ -18,7 +18,8 @@ from gpu_util import to_dev_bf16  # noqa: E402
 # (first shape, second and smaller shape); the default plans of these use the
 # scratch for split-K partials (16x2112x7168: 946,176 bytes; 8x2112x7168:
 # 473,088), for the pre-quantized A of the tiled kernel (1024x4096x4096:
-# 2,228,224; 512x4096x4096: 1,114,112) and of the pre-quantized plan
+# 2,228,224) and then of the stream kernel (512x4096x4096: 1,114,112), of
+# the pre-quantized plan
 # (768x2048x2048: 835,584; 600x3072x2048: 661,504), for the pre-quantized A
 # and the split partials of the stream kernel (32x8192x28672: 2,584,576;
 # 96x8192x8192: 417,792, no split), or not at all (64x7168x2048, 4x2880x512).
