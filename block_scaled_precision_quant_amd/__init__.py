@@ -258,6 +258,8 @@ def workspace_bytes(M, N, K, plan=None):
 
 def workspace_zero_bytes(M, N, K, plan=None):
     """Leading workspace bytes that must be zero before first use."""
+    if plan is None and (M == 0 or N == 0):
+        return 0  # an empty product needs no workspace
     p = plan if plan is not None else default_plan(M, N, K)
     cp = p._c()
     return int(load().mxfp4_plan_workspace_zero_bytes(ctypes.byref(cp), M, N, K))
@@ -330,14 +332,16 @@ def gemm_prequant(a_packed, M, b_packed, N, K, out=None, workspace=None, plan=No
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_packed.device)
     _matrix(out, "out", torch.bfloat16, M, N, like=a_packed)
-    p = plan if plan is not None else default_plan(M, N, K)
+    # an empty product (M or N = 0) has no plan; the call returns at once
+    p = plan if plan is not None or M == 0 or N == 0 else default_plan(M, N, K)
     workspace = _workspace(prequant_workspace_bytes(M, N, K, p), a_packed.device, workspace)
     if workspace is not None:
         _gpu(workspace, "workspace", like=a_packed)
-    cp = p._c()
+    cp = p._c() if p is not None else None
     _check(load().mxfp4_gemm_prequant(_ptr(a_packed), _nbytes(a_packed), _ptr(b_packed),
                                       _nbytes(b_packed), _ptr(out), out.stride(0), M, N, K,
                                       _ptr(workspace),
                                       _nbytes(workspace) if workspace is not None else 0,
-                                      ctypes.byref(cp), _stream(stream)))
+                                      ctypes.byref(cp) if cp is not None else None,
+                                      _stream(stream)))
     return out

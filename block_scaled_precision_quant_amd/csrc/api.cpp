@@ -79,13 +79,24 @@ mxfp4_plan make_plan(int mode, int mbw, int ntw, int wn, int wk, int ksw, int sp
   return p;
 }
 
-int check_gemm_shape(int M, int N, int K) {
-  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
-  if (N < 1) return fail(MXFP4_EINVAL, "N must be >= 1 (got %d)", N);
+// `call`: the shape of a GEMM call, where M or N may be 0 (an empty call,
+// which returns before this check); a plan needs both >= 1.
+int check_gemm_shape(int M, int N, int K, bool call = false) {
   if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  const int lo = call ? 0 : 1;
+  if (M < lo) return fail(MXFP4_EINVAL, "M must be >= %d (got %d)", lo, M);
+  if (N < lo) return fail(MXFP4_EINVAL, "N must be >= %d (got %d)", lo, N);
   if ((long long)M * K > (1LL << 40) || (long long)N * K > (1LL << 40) || (long long)M * N > (1LL << 40))
     return fail(MXFP4_EINVAL, "shape too large");
   return MXFP4_OK;
+}
+
+// An empty call: `rows` (M, or N where B's rows are the operand) or `cols`
+// (N of a product; 0 = none) is 0, the others are valid and K is a positive
+// multiple of 32.  There is nothing to read or write: the entry points
+// return success before looking at any pointer or launching anything.
+bool empty_call(int rows, int cols, int K) {
+  return rows >= 0 && cols >= 0 && (rows == 0 || cols == 0) && K >= 32 && K % 32 == 0;
 }
 
 // Tile width of a tiled plan: waves_n == 2 selects 256 x 128 tiles (four
@@ -534,12 +545,13 @@ size_t mxfp4_packed_bytes(int rows, int K) {
 
 int mxfp4_pack_b(const uint8_t* b_fp4, const uint8_t* b_scale, int N, int K, void* b_packed,
                  size_t b_packed_bytes, void* stream) {
+  if (empty_call(N, 1, K)) return ok();
   int rc;
   if ((rc = check_stream_ptrs(b_fp4, "b_fp4")) || (rc = check_stream_ptrs(b_scale, "b_scale")) ||
       (rc = check_stream_ptrs(b_packed, "b_packed")))
     return rc;
-  if (N < 1) return fail(MXFP4_EINVAL, "N must be >= 1 (got %d)", N);
   if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (N < 0) return fail(MXFP4_EINVAL, "N must be >= 0 (got %d)", N);
   if (!aligned(b_fp4, 16) || !aligned(b_packed, 16))
     return fail(MXFP4_EINVAL, "b_fp4 and b_packed must be 16-byte aligned");
   const size_t need = mxfp4_packed_bytes(N, K);
@@ -554,12 +566,13 @@ int mxfp4_pack_b(const uint8_t* b_fp4, const uint8_t* b_scale, int N, int K, voi
 
 int mxfp4_quant_a(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, int ld_fp4,
                   uint8_t* out_scale, int ld_scale, void* stream) {
+  if (empty_call(M, 1, K)) return ok();
   int rc;
   if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(out_fp4, "out_fp4")) ||
       (rc = check_stream_ptrs(out_scale, "out_scale")))
     return rc;
-  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
   if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (M < 0) return fail(MXFP4_EINVAL, "M must be >= 0 (got %d)", M);
   if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
   if (ld_fp4 < K / 2 || ld_fp4 % 4 != 0)
     return fail(MXFP4_EINVAL, "ld_fp4 must be >= K/2 and a multiple of 4 (got %d)", ld_fp4);
@@ -576,11 +589,12 @@ int mxfp4_quant_a(const uint16_t* a, int M, int K, int lda, uint8_t* out_fp4, in
 
 int mxfp4_quant_a_packed(const uint16_t* a, int M, int K, int lda, void* out_packed,
                          size_t out_packed_bytes, void* stream) {
+  if (empty_call(M, 1, K)) return ok();
   int rc;
   if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(out_packed, "out_packed")))
     return rc;
-  if (M < 1) return fail(MXFP4_EINVAL, "M must be >= 1 (got %d)", M);
   if (K < 32 || K % 32 != 0) return fail(MXFP4_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (M < 0) return fail(MXFP4_EINVAL, "M must be >= 0 (got %d)", M);
   if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
   if (!aligned(a, 16) || !aligned(out_packed, 16))
     return fail(MXFP4_EINVAL, "a and out_packed must be 16-byte aligned");
@@ -647,7 +661,7 @@ int check_gemm_args(const uint16_t* a, int lda, const void* b_packed, size_t b_p
   if ((rc = check_stream_ptrs(a, "a")) || (rc = check_stream_ptrs(b_packed, "b_packed")) ||
       (rc = check_stream_ptrs(c, "c")))
     return rc;
-  if ((rc = check_gemm_shape(M, N, K))) return rc;
+  if ((rc = check_gemm_shape(M, N, K, true))) return rc;
   if (lda < K || lda % 8 != 0) return fail(MXFP4_EINVAL, "lda must be >= K and a multiple of 8 (got %d)", lda);
   if (ldc < N) return fail(MXFP4_EINVAL, "ldc must be >= N (got %d)", ldc);
   if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 2))
@@ -692,6 +706,7 @@ extern "C" {
 int mxfp4_gemm_ex(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
                   uint16_t* c, int ldc, int M, int N, int K, void* workspace,
                   size_t workspace_bytes, const mxfp4_plan* plan, void* stream) {
+  if (empty_call(M, N, K)) return ok();
   int rc;
   if ((rc = check_gemm_args(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K))) return rc;
   const mxfp4_plan p = plan ? *plan : default_plan(M, N, K);
@@ -741,6 +756,7 @@ size_t mxfp4_gemm_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes;
 
 int mxfp4_gemm_noalloc(const uint16_t* a, int lda, const void* b_packed, size_t b_packed_bytes,
                        uint16_t* c, int ldc, int M, int N, int K, void* stream) {
+  if (empty_call(M, N, K)) return ok();
   int rc;
   if ((rc = check_gemm_args(a, lda, b_packed, b_packed_bytes, c, ldc, M, N, K))) return rc;
   const mxfp4_plan p = default_plan(M, N, K);
@@ -766,11 +782,12 @@ int mxfp4_gemm_prequant(const void* a_packed, size_t a_packed_bytes, const void*
                         size_t b_packed_bytes, uint16_t* c, int ldc, int M, int N, int K,
                         void* workspace, size_t workspace_bytes, const mxfp4_plan* plan,
                         void* stream) {
+  if (empty_call(M, N, K)) return ok();
   int rc;
   if ((rc = check_stream_ptrs(a_packed, "a_packed")) || (rc = check_stream_ptrs(b_packed, "b_packed")) ||
       (rc = check_stream_ptrs(c, "c")))
     return rc;
-  if ((rc = check_gemm_shape(M, N, K))) return rc;
+  if ((rc = check_gemm_shape(M, N, K, true))) return rc;
   if (ldc < N) return fail(MXFP4_EINVAL, "ldc must be >= N (got %d)", ldc);
   if (!aligned(a_packed, 16) || !aligned(b_packed, 16) || !aligned(c, 2))
     return fail(MXFP4_EINVAL, "a_packed and b_packed must be 16-byte aligned, c 2-byte aligned");

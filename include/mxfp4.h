@@ -27,6 +27,12 @@
  *     every buffer, and the size queries say how large each must be (the one
  *     exception, mxfp4_gemm_noalloc, uses a fixed array inside the library
  *     instead of a caller's workspace);
+ *   - an empty call -- M = 0 for the quantizers, N = 0 for mxfp4_pack_b,
+ *     M = 0 or N = 0 for the GEMMs, with K still a positive multiple of 32
+ *     -- returns 0 and enqueues nothing; its pointers and other arguments
+ *     are not read (they may be NULL).  The size queries give 0 for it;
+ *     mxfp4_default_plan and mxfp4_check_plan refuse it (an empty product
+ *     has no plan);
  *   - return value 0 is success; a negative value is one of MXFP4_E* below.
  *     On any error other than MXFP4_EHIP nothing has been enqueued.  The
  *     text of the last error of the calling thread is mxfp4_last_error();
@@ -88,7 +94,7 @@ size_t mxfp4_packed_bytes(int rows, int K);
  *   b_fp4   [N][K/2]  fp4x2, row-major, contiguous (16-byte aligned);
  *   b_scale [N][K/32] e8m0,  row-major, contiguous;
  *   b_packed  output, mxfp4_packed_bytes(N, K) bytes, 16-byte aligned.
- * Requires N >= 1, K >= 32, K % 32 == 0.  This is a byte permutation only
+ * Requires N >= 0 (0: an empty call), K >= 32, K % 32 == 0.  This is a byte permutation only
  * (no arithmetic).  Errors: ENULL, EINVAL, ESIZE, EHIP. */
 int mxfp4_pack_b(const uint8_t *b_fp4, const uint8_t *b_scale, int N, int K, void *b_packed,
                  size_t b_packed_bytes, void *stream);
@@ -98,7 +104,7 @@ int mxfp4_pack_b(const uint8_t *b_fp4, const uint8_t *b_scale, int N, int K, voi
  *   out_fp4  [M][ld_fp4] bytes, row m gets K/2 bytes, ld_fp4 >= K/2, ld_fp4 % 4 == 0,
  *            4-byte aligned;
  *   out_scale [M][ld_scale] bytes, row m gets K/32 bytes, ld_scale >= K/32.
- * Requires M >= 1, K >= 32, K % 32 == 0, lda >= K.  The group scale is the
+ * Requires M >= 0 (0: an empty call), K >= 32, K % 32 == 0, lda >= K.  The group scale is the
  * rule of submission 752099 `_bf16_to_fp4_hw`; elements round to nearest
  * e2m1 with ties to even and saturate at 6 (submission 694791).  Results are
  * bit-exact to that definition.  Errors: ENULL, EINVAL, EHIP. */
@@ -111,7 +117,7 @@ int mxfp4_quant_a(const uint16_t *a, int M, int K, int lda, uint8_t *out_fp4, in
  * read by the GEMM), with the scale and element rules of mxfp4_quant_a,
  * written in the GEMM's operand layout instead of a linear one.
  *   a  as for mxfp4_quant_a;  out_packed  mxfp4_packed_bytes(M, K) bytes,
- *   16-byte aligned.  Requires M >= 1, K >= 32, K % 32 == 0.  Applied to a
+ *   16-byte aligned.  Requires M >= 0 (0: an empty call), K >= 32, K % 32 == 0.  Applied to a
  *   weight matrix B [N][K] this is the one-time B preparation straight from
  *   bf16 (the same bytes as mxfp4_quant_a followed by mxfp4_pack_b).
  *   Errors: ENULL, EINVAL, ESIZE, EHIP. */
@@ -196,11 +202,14 @@ typedef struct mxfp4_plan {
 } mxfp4_plan;
 
 /* The plan mxfp4_gemm uses for a shape: a per-shape table for the tuned
- * shapes, otherwise the plan of least estimated time under a cost model
- * (fused, pre-quantized or, when M >= 256 and M and N give at least 16
- * tiles of 256 x 256, tiled with either tile width).  A tiled plan's
- * fields other than mode and waves_n are 1 and unused.
- * Errors: ENULL, EINVAL. */
+ * shapes; for M up to 512 against a B with K >= 4096, the stream mode or a
+ * fused plan that splits K, where measured rules take them; otherwise the
+ * plan of least estimated time under a cost model (fused, pre-quantized or,
+ * when M >= 256 and M and N give at least 16 tiles of 256 x 256, tiled with
+ * either tile width and K split over up to eight workgroups).  A tiled
+ * plan's fields other than mode, waves_n, split_k and split_reduce are 1
+ * and unused.
+ * Errors: ENULL, EINVAL (also for an empty shape). */
 int mxfp4_default_plan(int M, int N, int K, mxfp4_plan *plan);
 
 /* MXFP4_OK when `plan` is valid for the shape and has a compiled kernel;
@@ -244,7 +253,7 @@ size_t mxfp4_gemm_workspace_bytes(int M, int N, int K);
  *             bytes, 256-byte aligned (may be NULL when that is 0), whose
  *             leading zero-bytes (see mxfp4_plan_workspace_zero_bytes) were
  *             zero-filled once before first use.
- * Requires M >= 1, N >= 1, K >= 32, K % 32 == 0.
+ * Requires M >= 0, N >= 0 (either 0: an empty call), K >= 32, K % 32 == 0.
  * Inputs are finite.  c must not overlap a, b_packed or the workspace (the
  * kernels read the inputs while other workgroups already write C).
  * Errors: ENULL, EINVAL, ESIZE, EWORKSPACE, ENOTSUP, EHIP. */

@@ -74,6 +74,10 @@ static int host_checks(void) {
     CHECK(mxfp4_default_plan(32, 4096, 512, NULL) == MXFP4_ENULL, "NULL plan refused");
     CHECK(mxfp4_gemm(NULL, 512, NULL, 0, NULL, 4096, 32, 4096, 512, NULL, 0, NULL) == MXFP4_ENULL,
           "NULL pointers refused before any launch");
+    CHECK(mxfp4_gemm(NULL, 512, NULL, 0, NULL, 4096, 0, 4096, 512, NULL, 0, NULL) == MXFP4_OK,
+          "an empty call (M = 0) returns at once");
+    CHECK(mxfp4_quant_a(NULL, 0, 512, 512, NULL, 256, NULL, 16, NULL) == MXFP4_OK,
+          "an empty quantization returns at once");
     /* plan fields far out of range are refused without overflowing the
      * checks' arithmetic (the sanitizer build traps signed overflow) */
     mxfp4_plan huge = p; /* K = 512: 4 steps of 128 */

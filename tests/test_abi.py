@@ -69,8 +69,8 @@ def test_gemm_rejects_bad_arguments(lib):
     assert f(None, 512, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == ENULL
     assert f(FAKE, 512, None, nb, FAKE, 32, 4, 32, 512, None, 0, None) == ENULL
     assert f(FAKE, 512, FAKE, nb, None, 32, 4, 32, 512, None, 0, None) == ENULL
-    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 0, 32, 512, None, 0, None) == EINVAL  # M
-    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 0, 512, None, 0, None) == EINVAL   # N
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, -1, 32, 512, None, 0, None) == EINVAL  # M
+    assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, -1, 512, None, 0, None) == EINVAL   # N
     assert f(FAKE, 512, FAKE, nb, FAKE, 32, 4, 32, 500, None, 0, None) == EINVAL  # K % 32
     assert f(FAKE, 256, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda < K
     assert f(FAKE, 516, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # lda % 8
@@ -79,6 +79,39 @@ def test_gemm_rejects_bad_arguments(lib):
     odd = ctypes.c_void_p(0x10008)
     assert f(odd, 512, FAKE, nb, FAKE, 32, 4, 32, 512, None, 0, None) == EINVAL  # alignment
     assert f(FAKE, 512, FAKE, nb - 1, FAKE, 32, 4, 32, 512, None, 0, None) == ESIZE
+
+
+def test_empty_calls_return_at_once(lib):
+    """M = 0 or N = 0 is an empty product: each entry point returns 0 before
+    it reads a pointer or launches anything (so NULL pointers pass, and this
+    is safe with or without a GPU).  K must still be a positive multiple of
+    32 and sizes below zero are refused; an empty shape has no plan and needs
+    no workspace."""
+    K = 512
+    for M, N in ((0, 32), (4, 0), (0, 0)):
+        assert lib.mxfp4_gemm(None, 0, None, 0, None, 0, M, N, K, None, 0, None) == 0
+        assert lib.mxfp4_gemm_ex(None, 0, None, 0, None, 0, M, N, K, None, 0, None, None) == 0
+        assert lib.mxfp4_gemm_noalloc(None, 0, None, 0, None, 0, M, N, K, None) == 0
+        assert lib.mxfp4_gemm_prequant(None, 0, None, 0, None, 0, M, N, K, None, 0, None,
+                                       None) == 0
+        assert lib.mxfp4_gemm_workspace_bytes(M, N, K) == 0
+        assert lib.mxfp4_gemm_prequant_workspace_bytes(None, M, N, K) == 0
+        assert lib.mxfp4_default_plan(M, N, K, ctypes.byref(mx._CPlan())) == EINVAL
+    assert lib.mxfp4_quant_a(None, 0, K, 0, None, 0, None, 0, None) == 0
+    assert lib.mxfp4_quant_a_packed(None, 0, K, 0, None, 0, None) == 0
+    assert lib.mxfp4_pack_b(None, None, 0, K, None, 0, None) == 0
+    assert lib.mxfp4_packed_bytes(0, K) == 0
+    # an empty call with a bad K or a negative size is an error like any other
+    nb = mx.packed_bytes(32, 512)
+    assert lib.mxfp4_gemm(FAKE, 512, FAKE, nb, FAKE, 32, 0, 32, 500, None, 0, None) == EINVAL
+    assert b"K must be" in lib.mxfp4_last_error()
+    assert lib.mxfp4_gemm(FAKE, 512, FAKE, nb, FAKE, 32, -1, 0, 512, None, 0, None) == EINVAL
+    assert lib.mxfp4_quant_a(FAKE, 0, 0, 512, FAKE, 256, FAKE, 16, None) == EINVAL
+    assert lib.mxfp4_quant_a(FAKE, -1, 512, 512, FAKE, 256, FAKE, 16, None) == EINVAL
+    assert b"M must be >= 0" in lib.mxfp4_last_error()
+    assert lib.mxfp4_quant_a_packed(FAKE, 0, 500, 512, FAKE, 1 << 20, None) == EINVAL
+    assert lib.mxfp4_pack_b(FAKE, FAKE, 0, 16, FAKE, 1 << 20, None) == EINVAL
+    assert lib.mxfp4_pack_b(FAKE, FAKE, -2, 512, FAKE, 1 << 20, None) == EINVAL
 
 
 def test_plan_checks(lib):
@@ -301,7 +334,7 @@ def test_workspace_sizes(lib):
 def test_quant_and_pack_reject_bad_arguments(lib):
     q = lib.mxfp4_quant_a
     assert q(None, 4, 512, 512, FAKE, 256, FAKE, 16, None) == ENULL
-    assert q(FAKE, 0, 512, 512, FAKE, 256, FAKE, 16, None) == EINVAL
+    assert q(FAKE, -4, 512, 512, FAKE, 256, FAKE, 16, None) == EINVAL  # M
     assert q(FAKE, 4, 48, 48, FAKE, 24, FAKE, 2, None) == EINVAL      # K % 32
     assert q(FAKE, 4, 512, 512, FAKE, 128, FAKE, 16, None) == EINVAL  # ld_fp4 < K/2
     assert q(FAKE, 4, 512, 512, FAKE, 256, FAKE, 8, None) == EINVAL   # ld_scale < K/32
@@ -309,7 +342,7 @@ def test_quant_and_pack_reject_bad_arguments(lib):
     assert qp(FAKE, 4, 512, 512, FAKE, mx.packed_bytes(4, 512) - 1, None) == ESIZE
     assert qp(FAKE, 4, 100, 104, FAKE, 1 << 20, None) == EINVAL       # K % 32
     pb = lib.mxfp4_pack_b
-    assert pb(FAKE, FAKE, 0, 512, FAKE, 1 << 20, None) == EINVAL      # N
+    assert pb(FAKE, FAKE, -1, 512, FAKE, 1 << 20, None) == EINVAL     # N
     assert pb(FAKE, FAKE, 32, 512, FAKE, mx.packed_bytes(32, 512) - 1, None) == ESIZE
     assert pb(FAKE, None, 32, 512, FAKE, 1 << 20, None) == ENULL
 
