@@ -38,6 +38,10 @@ WIDTHS = pytest.mark.parametrize("plan", [TILED, TILED128], ids=["w256", "w128"]
     (2048, 1040, 2080),
     (300, 280, 384),    # 3 K steps: only the steps after the last group of four
     (520, 512, 800),    # 7 K steps, the last partial: one group of four, then 3
+    # the copies' cache policy follows the grid: at most four row tiles
+    # stream B nontemporal, at most eight column tiles stream A
+    (1300, 1000, 1024),  # 6 row tiles, 4 or 8 column tiles: A nontemporal, B not
+    (520, 2200, 512),    # 3 row tiles, 9 or 18 column tiles: B nontemporal, A not
 ])
 @WIDTHS
 def test_tiled_full_oracle(M, N, K, plan):
