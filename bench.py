@@ -58,6 +58,11 @@ PAGES_CONTEXT = {
     "source": "kernelindex.com kernelbot-amd-mxfp4-mm-705642, v3 docstring (anatomy of the "
               "library baseline at M=4): about 8.2 us per call against a memory floor of "
               "about 0.13 us; context only",
+    "hip_fused_quant_split_k_us_m64": 10.0,
+    "source_m64": "kernelindex.com kernelbot-amd-mxfp4-mm-739530, v5 HIP source, the comment "
+                  "heading the fused-quant split-K kernel (fgemm_fq): about 10.0 us per call at "
+                  "m=64, shape not stated (the pages' one m=64 benchmark shape is "
+                  "64x7168x2048); context only",
 }
 
 
