@@ -143,3 +143,47 @@ def test_stream_mode_large_sampled(M, N, K, mbw, ntw, steps):
     assert not torch.isnan(c).any().item()
     del c, b_packed, dev_a
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mbw,ntw,steps", [(4, 2, 1 << 15), (1, 1, 4096)],
+                         ids=["whole_k", "split8"])
+def test_stream_max_k_sampled(mbw, ntw, steps):
+    """K at the stream mode's limit (2^22, 32768 K steps: the largest offsets
+    the per-workgroup buffer descriptors carry), ragged M and N, with the
+    whole of K in one workgroup (four row blocks, two tiles per wavefront)
+    or split eight ways.  Elements are integers in [-2, 2] (drawn on the GPU
+    from a seeded generator): they quantize exactly, every product is an
+    integer of magnitude <= 4 and every partial sum an integer of magnitude
+    <= 2^24, so the fp32 sums of the oracle and of the kernel are exact in
+    any order and the usual tolerance measures the kernel alone.  B is
+    prepared by the packed quantizer (bit-exact to the oracle's quantization
+    in test_gpu_quant); the oracle quantizes the sampled bf16 rows itself."""
+    M, N, K = 40, 136, 1 << 22
+    plan = stream_plan(mbw, ntw, steps, M, N, K)
+    print("case stream max K", M, N, K, plan, flush=True)
+    mx.check_plan(plan, M, N, K)
+    gen = torch.Generator(device="cuda").manual_seed(4194305)
+    a = torch.randint(-2, 3, (M, K), generator=gen, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b = torch.randint(-2, 3, (N, K), generator=gen, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b_packed = mx.quant_a_packed(b)
+    rows = np.array([0, 1, 15, 16, 39])
+    cols = np.array([0, 15, 63, 64, 127, 128, 135])
+
+    def host_bits(t, idx):
+        return t[torch.as_tensor(idx, device=t.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+
+    b_rows = host_bits(b, cols)
+    del b
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mx.gemm(a, b_packed, N, out=c, plan=plan)
+    torch.cuda.synchronize()
+    aq, asc = oracle.quantize(host_bits(a, rows))
+    bq, bsc = oracle.quantize(b_rows)
+    want, want64 = oracle.gemm(oracle.dequantize(aq, asc), oracle.dequantize(bq, bsc))
+    assert np.array_equal(want.astype(np.float64), want64)  # the sums are exact
+    r = torch.as_tensor(rows, device=c.device)
+    q = torch.as_tensor(cols, device=c.device)
+    assert_close_to_oracle(bf16_out_to_f32(c[r][:, q]), want, "stream max K")
+    assert not torch.isnan(c).any().item()
+    del a, c, b_packed
+    torch.cuda.empty_cache()
