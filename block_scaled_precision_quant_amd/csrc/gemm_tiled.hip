@@ -377,27 +377,36 @@ void gemm_tiled_kernel(TiledArgs g) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every stage read done
     __builtin_amdgcn_sched_barrier(0);
     const int wrow = (lane & 31) * kPitch + 8 * (lane >> 5);
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x2 lo = {acc[u][v][4 * q], acc[u][v][4 * q + 1]};
-          const f32x2 hi = {acc[u][v][4 * q + 2], acc[u][v][4 * q + 3]};
-          const uint2 w = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
-                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2)));
-          *reinterpret_cast<uint2*>(stage + wrow + 32 * u * kPitch + 2 * (32 * v + 8 * q)) = w;
-        }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wavefront's own rows, lanes exchanged
     const int rsub = lane >> 3, cchunk = lane & 7;
-#pragma unroll 8
-    for (int i = 0; i < 4 * kU; ++i) {
-      const int r = 8 * i + rsub;
-      const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
-      if (row0 + r < g.M)
-        __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w},
-                                    reinterpret_cast<u32x4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk));
+    // With 128 x 64 blocks (kU == 4) one 32-row block at a time: its rows
+    // staged, then read back and stored while the next block is staged, so
+    // the LDS writes overlap the stores (1-5 % less time per 256 x 256-tile
+    // kernel at 2048x4096x4096 to 8192^3, the same bits); 64 x 64 blocks
+    // stage all their rows first (no gain measured there).
+    constexpr int kBlk = kU == 4 ? 1 : kU;
+#pragma unroll
+    for (int u0 = 0; u0 < kU; u0 += kBlk) {
+#pragma unroll
+      for (int u = u0; u < u0 + kBlk; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x2 lo = {acc[u][v][4 * q], acc[u][v][4 * q + 1]};
+            const f32x2 hi = {acc[u][v][4 * q + 2], acc[u][v][4 * q + 3]};
+            const uint2 w = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                       __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2)));
+            *reinterpret_cast<uint2*>(stage + wrow + 32 * u * kPitch + 2 * (32 * v + 8 * q)) = w;
+          }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // these rows staged, lanes exchanged
+#pragma unroll
+      for (int i = 4 * u0; i < 4 * (u0 + kBlk); ++i) {
+        const int r = 8 * i + rsub;
+        const uint4 d = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * cchunk);
+        if (row0 + r < g.M)
+          __builtin_nontemporal_store(u32x4{d.x, d.y, d.z, d.w},
+                                      reinterpret_cast<u32x4*>(g.c + (size_t)(row0 + r) * g.ldc + col0 + 8 * cchunk));
+      }
     }
   } else {
     const int lrow0 = row0 + (lane & 31);
